@@ -1,0 +1,446 @@
+"""Pins for the CPU oracle: checks against facts fixed by the pages, by the
+format specifications and by mathematics, never against the oracle itself.
+
+Each ``check_*`` takes a loaded oracle library (so the same checks can be
+run against deliberately broken copies of the oracle) and raises
+AssertionError on failure.
+"""
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U32 = 2.0 ** -24  # unit roundoff of binary32
+
+
+def gamma(d):
+    return d * U32 / (1.0 - d * U32)
+
+
+# ------------------------------------------------------------- conversions --
+
+def check_f16_decode_all(lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = np.array([lib.orc_f16_to_f32(int(b)) for b in bits], np.float32)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _interesting_f32(g, n):
+    # wide exponent sweep, fp16 halfway points, overflow and subnormal borders
+    e = g.integers(-30, 20, size=n)
+    m = g.uniform(1.0, 2.0, size=n)
+    v = (np.ldexp(m, e) * np.where(g.random(n) < 0.5, -1.0, 1.0)).astype(np.float32)
+    h = g.integers(0, 0x7C00, size=n // 4).astype(np.uint16).view(np.float16).astype(np.float64)
+    halfway = (h + np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(h), 2.0 ** -24))).astype(int) - 11)
+               ).astype(np.float32)
+    specials = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 65536.0, 2.0 ** -24, 2.0 ** -25,
+                         2.0 ** -25 * 1.5, 2.0 ** -14, 2.0 ** -14 * (1 - 2.0 ** -11), 1e-30, 1e30],
+                        np.float32)
+    return np.concatenate([v, halfway, specials, -specials])
+
+
+def check_f32_to_f16_rne(lib):
+    g = np.random.default_rng(11)
+    v = _interesting_f32(g, 20000)
+    ours = np.array([lib.orc_f32_to_f16(float(a)) for a in v], np.uint16)
+    ref = v.astype(np.float16).view(np.uint16)  # numpy: IEEE round-to-nearest-even
+    assert np.array_equal(ours, ref), np.flatnonzero(ours != ref)[:10]
+
+
+def check_f64_to_f16_rne(lib):
+    g = np.random.default_rng(12)
+    v = np.concatenate([g.standard_normal(5000), np.ldexp(g.uniform(1, 2, 5000), g.integers(-28, 17, 5000))])
+    ours = np.array([lib.orc_f64_to_f16(float(a)) for a in v], np.uint16)
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def check_f32_to_bf16_rne(lib):
+    import torch
+    g = np.random.default_rng(13)
+    v = np.concatenate([
+        (np.ldexp(g.uniform(1, 2, 20000), g.integers(-140, 127, 20000))
+         * np.where(g.random(20000) < 0.5, -1, 1)).astype(np.float32),
+        # exact halfway points between adjacent bf16 values
+        ((g.integers(0, 0x7F00, 4000).astype(np.uint32) << 16) | 0x8000).view(np.float32),
+        np.array([0.0, -0.0, 3.3895314e38, 3.4028235e38, 1e-40, 1e-45], np.float32),
+    ])
+    ours = np.array([lib.orc_f32_to_bf16(float(a)) for a in v], np.uint16)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref), np.flatnonzero(ours != ref)[:10]
+
+
+def check_bf16_decode(lib):
+    bits = np.arange(0, 65536, 7, dtype=np.uint32)
+    ours = np.array([lib.orc_bf16_to_f32(int(b)) for b in bits], np.float32)
+    ref = (bits << 16).view(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+# ----------------------------------------------------------------- decode --
+
+def check_int2_decode(lib):
+    import ctypes as C
+    a, b = (C.c_int8 * 4)(), (C.c_int8 * 4)()
+    for byte in range(256):
+        lib.orc_int2_decode_byte_lut(byte, C.cast(a, C.c_void_p))
+        lib.orc_int2_decode_byte_arith(byte, C.cast(b, C.c_void_p))
+        assert list(a) == list(b), byte
+        # two's-complement reading of each 2-bit field, low field first
+        for t in range(4):
+            f = (byte >> (2 * t)) & 3
+            assert a[t] == (f if f < 2 else f - 4), (byte, t)
+    # worked bytes: 0xE4 = fields 0,1,2,3 (low first) -> 0, 1, -2, -1
+    lib.orc_int2_decode_byte_arith(0xE4, C.cast(a, C.c_void_p))
+    assert list(a) == [0, 1, -2, -1]
+    lib.orc_int2_decode_byte_lut(0x00, C.cast(a, C.c_void_p))
+    assert list(a) == [0, 0, 0, 0]
+    lib.orc_int2_decode_byte_lut(0xFF, C.cast(a, C.c_void_p))
+    assert list(a) == [-1, -1, -1, -1]
+    vals = sorted({lib.orc_int2_value(f) for f in range(4)})
+    assert vals == [-2, -1, 0, 1]
+
+
+def check_int4_decode(lib):
+    import ctypes as C
+    out = (C.c_int8 * 2)()
+    seen = []
+    for byte in range(256):
+        lib.orc_int4_decode_byte_arith(byte, C.cast(out, C.c_void_p))
+        lut = [lib.orc_int4_value(byte & 15), lib.orc_int4_value(byte >> 4)]
+        assert list(out) == lut, byte
+        seen += lut
+    # symmetric code-8: every value -8..7 once per nibble position, 0 at code 8
+    assert sorted(set(seen)) == list(range(-8, 8))
+    assert lib.orc_int4_value(8) == 0 and lib.orc_int4_value(0) == -8 and lib.orc_int4_value(15) == 7
+
+
+def check_e2m1_table(lib):
+    # OCP MX v1.0 E2M1: exponent bias 1, one mantissa bit, subnormal at exponent 0
+    for nib in range(16):
+        s, e, m = nib >> 3, (nib >> 1) & 3, nib & 1
+        mag = 0.5 * m if e == 0 else math.ldexp(1.0 + 0.5 * m, e - 1)
+        want = -mag if s else mag
+        got = lib.orc_e2m1_value(nib)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), nib
+    for e in range(255):
+        assert lib.orc_e8m0_value(e) == math.ldexp(1.0, e - 127), e
+    assert math.isnan(lib.orc_e8m0_value(255))
+
+
+def check_pack_roundtrip(lib):
+    g = np.random.default_rng(21)
+    v = g.integers(-2, 2, size=(5, 192)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_int2(oracle.pack_int2(v, lib), 192, lib), v)
+    q = g.integers(0, 16, size=(5, 96)).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(q, lib), 96, lib), q)
+    nb = g.integers(0, 16, size=(5, 96)).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_e2m1(oracle.pack_e2m1(nb, lib), 96, lib), nb)
+    # every code at every position: little-endian fields along K
+    for i in range(16):
+        for c in (-2, -1, 1):
+            row = np.zeros((1, 16), np.int8)
+            row[0, i] = c
+            assert int(oracle.pack_int2(row, lib)[0, 0]) == ((c & 3) << (2 * i))
+    for i in range(8):
+        for q0 in (1, 7, 15):
+            row = np.zeros((1, 8), np.uint8)
+            row[0, i] = q0
+            assert int(oracle.pack_int4(row, lib)[0, 0]) == (q0 << (4 * i))
+    for k in range(2):
+        row = np.zeros((1, 2), np.uint8)
+        row[0, k] = 0xB
+        assert int(oracle.pack_e2m1(row, lib)[0, 0]) == (0xB << (4 * k))
+
+
+# --------------------------------------------------------------- products --
+
+def check_products_exact():
+    """The products the fixed order relies on are exact in binary32, so a
+    fused multiply-add and a multiply-then-add give the same bits."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    h = h[np.isfinite(h)].astype(np.float32)
+    for c in list(range(-8, 8)):
+        p32 = (np.float32(c) * h).astype(np.float64)
+        p64 = np.float64(c) * h.astype(np.float64)
+        assert np.array_equal(p32, p64), c
+    b = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    b = b[np.isfinite(b)]
+    for v in (0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.5, -6.0):
+        p32 = np.float32(v) * b
+        p64 = np.float64(v) * b.astype(np.float64)
+        ok = np.abs(p64) <= np.finfo(np.float32).max
+        assert np.array_equal(p32[ok].astype(np.float64), p64[ok]), v
+
+
+# --------------------------------------------------------------- FO sums ---
+
+def _tiny_cases():
+    g = np.random.default_rng(31)
+    for K in (64, 128, 192, 1536):
+        for M, N in ((1, 1), (2, 7), (3, 5)):
+            yield g, M, N, K
+
+
+def check_int2_vs_fp64(lib):
+    for g, M, N, K in _tiny_cases():
+        wq = synth.raw_words(g, (N, K // 16))
+        sc = synth.f16_bits(g.uniform(0.01, 0.05, N))
+        x = synth.f16_bits(g.standard_normal((M, K)) * 4)
+        y = oracle.qmv_int2(wq, sc, x, lib=lib)
+        y64, a = oracle.ref64_int2(wq, sc, x, lib=lib)
+        d = 63 + math.ceil(math.log2(K // 64)) if K > 64 else 63
+        bound = gamma(d) * a * (1 + U32) + U32 * np.abs(y64) + 1e-12 * a
+        assert np.all(np.abs(y - y64) <= bound), (K, M, N, np.max(np.abs(y - y64) - bound))
+
+
+def check_int4_vs_fp64(lib):
+    for g, M, N, K in _tiny_cases():
+        wq = synth.raw_words(g, (N, K // 8))
+        sc = synth.f16_bits(g.uniform(0.005, 0.02, (N, K // 32)))
+        x = synth.f16_bits(g.standard_normal((M, K)) * 4)
+        y = oracle.qmv_int4(wq, sc, x, lib=lib)
+        y64, a = oracle.ref64_int4(wq, sc, x, lib=lib)
+        d = 31 + 1 + math.ceil(math.log2(K // 32))
+        bound = gamma(d) * a + 1e-12 * a
+        assert np.all(np.abs(y - y64) <= bound), (K, M, N, np.max(np.abs(y - y64) - bound))
+
+
+def check_mxfp4_vs_fp64(lib):
+    for g, M, N, K in _tiny_cases():
+        wq = synth.raw_bytes(g, (N, K // 2))
+        e = (127 + g.integers(-8, 3, (N, K // 32))).astype(np.uint8)
+        x = synth.bf16_bits(g.standard_normal((M, K)) * 4)
+        y = oracle.qmm_mxfp4(wq, e, x, lib=lib)
+        y64, a = oracle.ref64_mxfp4(wq, e, x, lib=lib)
+        d = 31 + 1 + math.ceil(math.log2(K // 32))
+        bound = gamma(d) * a + 1e-12 * a
+        assert np.all(np.abs(y - y64) <= bound), (K, M, N, np.max(np.abs(y - y64) - bound))
+
+
+def check_integer_x_exact(lib):
+    """Integer-valued x with power-of-two scales: every partial sum is exact,
+    so any order equals the exact dot product."""
+    g = np.random.default_rng(41)
+    for K in (64, 192, 1536):
+        M, N = 2, 6
+        x = synth.f16_bits(g.integers(-8, 9, (M, K)).astype(np.float64))
+        wq = synth.raw_words(g, (N, K // 16))
+        sc = synth.f16_bits(np.ldexp(1.0, g.integers(-4, 3, N)))
+        y = oracle.qmv_int2(wq, sc, x, lib=lib)
+        y64, _ = oracle.ref64_int2(wq, sc, x, lib=lib)
+        assert np.array_equal(y.astype(np.float64), y64)
+        wq4 = synth.raw_words(g, (N, K // 8))
+        sc4 = synth.f16_bits(np.ldexp(1.0, g.integers(-4, 3, (N, K // 32))))
+        y = oracle.qmv_int4(wq4, sc4, x, lib=lib)
+        y64, _ = oracle.ref64_int4(wq4, sc4, x, lib=lib)
+        assert np.array_equal(y.astype(np.float64), y64)
+        xb = synth.bf16_bits(g.integers(-8, 9, (M, K)).astype(np.float64))
+        wq8 = synth.raw_bytes(g, (N, K // 2))
+        e = (127 + g.integers(-8, 3, (N, K // 32))).astype(np.uint8)
+        y = oracle.qmm_mxfp4(wq8, e, xb, lib=lib)
+        y64, _ = oracle.ref64_mxfp4(wq8, e, xb, lib=lib)
+        assert np.array_equal(y.astype(np.float64), y64)
+
+
+def check_single_segment_sequential(lib):
+    """With one segment per row the fixed order is a plain running sum in
+    code order (numpy's cumulative sum in float32), then the row scale."""
+    g = np.random.default_rng(51)
+    x = synth.f16_bits(g.standard_normal((1, 64)) * 100)
+    vals = g.integers(-2, 2, (3, 64)).astype(np.int8)
+    wq = oracle.pack_int2(vals, lib)
+    sc = synth.f16_bits(g.uniform(0.01, 0.05, 3))
+    y = oracle.qmv_int2(wq, sc, x, lib=lib)
+    xf = x.view(np.float16).astype(np.float32)[0]
+    for n in range(3):
+        run = np.cumsum(vals[n].astype(np.float32) * xf, dtype=np.float32)[-1]
+        assert y[0, n] == np.float32(sc.view(np.float16)[n]) * run
+    # int4: one group of 32, value q-8, then the group scale
+    x = synth.f16_bits(g.standard_normal((1, 32)) * 100)
+    q = g.integers(0, 16, (3, 32)).astype(np.uint8)
+    sc = synth.f16_bits(g.uniform(0.005, 0.02, (3, 1)))
+    y = oracle.qmv_int4(oracle.pack_int4(q, lib), sc, x, lib=lib)
+    xf = x.view(np.float16).astype(np.float32)[0]
+    for n in range(3):
+        run = np.cumsum((q[n].astype(np.float32) - 8) * xf, dtype=np.float32)[-1]
+        assert y[0, n] == np.float32(sc.view(np.float16)[n, 0]) * run
+
+
+def _golden_row(case):
+    K = case["K"]
+    codes = np.zeros((1, K), np.int8)
+    x = np.zeros((1, K), np.float64)
+    if "segments" in case:
+        for j, tag in enumerate(case["segments"]):
+            base = 64 * j
+            if tag in ("A", "-A"):
+                codes[0, base:base + 33] = -2
+                x[0, base:base + 33] = -65504.0 if tag == "A" else 65504.0
+            elif tag == "s":
+                codes[0, base + 1] = 1
+                x[0, base + 1] = 0.125
+    else:
+        for ent in case["entries"]:
+            k0, k1 = ent["k"]
+            codes[0, k0:k1 + 1] = ent["code"]
+            x[0, k0:k1 + 1] = ent["x"]
+    return codes, synth.f16_bits(x)
+
+
+def check_golden_order(lib):
+    with open(os.path.join(GOLDEN, "fo_order_int2.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        codes, x = _golden_row(case)
+        wq = oracle.pack_int2(codes, lib)
+        sc = synth.f16_bits(np.array([1.0]))
+        y = oracle.qmv_int2(wq, sc, x, lib=lib)
+        assert y[0, 0] == np.float32(case["expected_y"]), (case["name"], y[0, 0])
+
+
+def check_threads_identical(lib):
+    d = synth.int2_inputs(2, 333, 1536, salt=9)
+    a = oracle.qmv_int2(d["wq"], d["scale"], d["x"], threads=1, lib=lib)
+    b = oracle.qmv_int2(d["wq"], d["scale"], d["x"], threads=7, lib=lib)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    d = synth.mxfp4_inputs(2, 101, 5376, salt=9)
+    a = oracle.qmm_mxfp4(d["wq"], d["e8m0"], d["x"], threads=1, lib=lib)
+    b = oracle.qmm_mxfp4(d["wq"], d["e8m0"], d["x"], threads=5, lib=lib)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------ exp / GELU ---
+
+def _ulp32(v):
+    v = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 23).astype(int))
+
+
+def check_exp_accuracy(lib):
+    z = np.concatenate([np.linspace(-87, 87, 200001), np.linspace(-1, 1, 20001)]).astype(np.float32)
+    ours = np.array([lib.orc_exp(float(a)) for a in z], np.float64)
+    ref = np.exp(z.astype(np.float64))
+    err = np.abs(ours - ref) / _ulp32(ref)
+    assert err.max() <= 2.0, err.max()
+    assert lib.orc_exp(0.0) == 1.0
+
+
+def check_gelu_accuracy(lib):
+    g = np.linspace(-10, 10, 100001).astype(np.float32)
+    ours = np.array([lib.orc_gelu(float(a)) for a in g], np.float64)
+    gd = g.astype(np.float64)
+    u = math.sqrt(2.0 / math.pi) * (gd + 0.044715 * gd ** 3)
+    # g * (1 + tanh u) / 2 written as g / (1 + e^(-2u)), which double evaluates
+    # without cancellation for negative g
+    ref = gd / (1.0 + np.exp(-2.0 * u))
+    # where -2u > 87 the definition clamps the exponent: |result| < |g| e^-87
+    slack = np.where(-2.0 * u > 87.0, 2.0 * np.abs(gd) * math.exp(-87.0), 0.0)
+    # the binary32 argument -2u carries ~3 roundings, so e^(-2u) is only
+    # known to |2u| * 3u32 relative: the condition of the exponential
+    cond = 4.0 * np.abs(2.0 * u) * U32 * np.abs(ref)
+    err = (np.abs(ours - ref) - slack - cond) / _ulp32(ref)
+    assert err.max() <= 8.0, err.max()
+    assert lib.orc_gelu(0.0) == 0.0
+
+
+# -------------------------------------------------------------- RMSNorm ----
+
+def check_rmsnorm_vs_fp64(lib):
+    for K in (64, 1536, 4096):
+        d = synth.fused_inputs(1, 8, K, salt=K)
+        x, r, gm = d["x"][0], d["residual"][0], d["gamma"]
+        h, xn, inv = oracle.rmsnorm_prologue(x, r, gm, 1e-6, lib=lib)
+        xd = x.view(np.float16).astype(np.float64)
+        rd = r.view(np.float16).astype(np.float64)
+        h_ref = (xd + rd).astype(np.float16)  # one rounding of the exact sum
+        assert np.array_equal(h, h_ref.view(np.uint16))
+        hd = h_ref.astype(np.float64)
+        inv64 = 1.0 / math.sqrt(np.sum(hd * hd) / K + float(np.float32(1e-6)))
+        d_ = 63 + math.ceil(math.log2(max(K // 64, 1))) + 4
+        assert abs(float(inv) - inv64) <= gamma(d_) * inv64
+        xn64 = hd * inv64 * gm.view(np.float16).astype(np.float64)
+        got = xn.view(np.float16).astype(np.float64)
+        # within one fp16 ulp (the fp32 steps are within a few binary32 ulps)
+        ulp16 = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(xn64), 2.0 ** -14))).astype(int) - 10)
+        assert np.all(np.abs(got - xn64) <= ulp16), np.max(np.abs(got - xn64) / ulp16)
+
+
+def check_fused_composition(lib):
+    d = synth.fused_inputs(2, 40, 1536, salt=3)
+    out, res, g, u = oracle.int2_rmsnorm_gateup_gelu(
+        d["x"], d["residual"], d["gamma"], d["eps"], d["wq_gate"], d["s_gate"], d["wq_up"],
+        d["s_up"], lib=lib)
+    # fp64 composition: normalise, dequantize, dot, GELU (tanh form), product
+    for m in range(2):
+        xd = d["x"][m].view(np.float16).astype(np.float64)
+        rd = d["residual"][m].view(np.float16).astype(np.float64)
+        hd = (xd + rd).astype(np.float16).astype(np.float64)
+        assert np.array_equal(res[m], (xd + rd).astype(np.float16).view(np.uint16))
+        xn = hd / math.sqrt(np.mean(hd * hd) + 1e-6) * d["gamma"].view(np.float16).astype(np.float64)
+        xn16 = xn.astype(np.float16)
+        wg = oracle.unpack_int2(d["wq_gate"], 1536, lib).astype(np.float64)
+        wu = oracle.unpack_int2(d["wq_up"], 1536, lib).astype(np.float64)
+        gd = (wg @ xn16.astype(np.float64)) * d["s_gate"].view(np.float16).astype(np.float64)
+        ud = (wu @ xn16.astype(np.float64)) * d["s_up"].view(np.float16).astype(np.float64)
+        # gate/up within a loose bound of the fp64 path (xn may differ by 1 fp16 ulp)
+        assert np.max(np.abs(g[m] - gd)) <= 2e-3 * np.max(np.abs(gd)) + 1e-3
+        assert np.max(np.abs(u[m] - ud)) <= 2e-3 * np.max(np.abs(ud)) + 1e-3
+        gel = 0.5 * gd * (1 + np.tanh(math.sqrt(2 / math.pi) * (gd + 0.044715 * gd ** 3)))
+        o = out[m].view(np.float16).astype(np.float64)
+        ref = gel * ud
+        assert np.max(np.abs(o - ref)) <= 5e-3 * np.max(np.abs(ref)) + 1e-3
+
+
+# --------------------------------------------------------------- argmax ----
+
+def check_argmax_ties(lib):
+    g = np.random.default_rng(61)
+    K, N = 128, 50
+    vals = g.integers(-2, 2, (N, K)).astype(np.int8)
+    x = synth.f16_bits(g.standard_normal((1, K)))
+    sc = synth.f16_bits(np.full(N, 0.03))
+    _, _, logits = oracle.int2_argmax(oracle.pack_int2(vals, lib), sc, x, lib=lib)
+    best = int(np.argmax(logits[0]))
+    # duplicate the winning row at a higher index: the lower index must win
+    v2 = vals.copy()
+    v2[N - 1] = vals[best]
+    idx, mv, lg = oracle.int2_argmax(oracle.pack_int2(v2, lib), sc, x, lib=lib)
+    assert int(idx[0]) == min(best, N - 1) and mv[0] == lg[0, idx[0]]
+    # duplicate at a lower index: that index wins
+    lo = 0 if best != 0 else 1
+    v3 = vals.copy()
+    v3[lo] = vals[best]
+    idx, _, _ = oracle.int2_argmax(oracle.pack_int2(v3, lib), sc, x, lib=lib)
+    assert int(idx[0]) == min(lo, best)
+    # all-zero logits, some rows with negative scale (-0 results): index 0
+    z = np.zeros((N, K), np.int8)
+    scz = synth.f16_bits(np.where(np.arange(N) % 2 == 0, -0.03, 0.03))
+    idx, mv, lg = oracle.int2_argmax(oracle.pack_int2(z, lib), scz, x, lib=lib)
+    assert np.signbit(lg[0, 0]) and int(idx[0]) == 0 and mv[0] == 0.0
+    # against numpy's argmax (first occurrence) on the oracle's own logits, M = 4
+    d = synth.int2_inputs(4, 3000, 256, salt=2)
+    idx, mv, lg = oracle.int2_argmax(d["wq"], d["scale"], d["x"], lib=lib)
+    assert np.array_equal(idx, np.argmax(lg, axis=1).astype(np.int32))
+    assert np.array_equal(mv, lg.max(axis=1))
+
+
+ALL_CHECKS = [
+    check_f16_decode_all, check_f32_to_f16_rne, check_f64_to_f16_rne, check_f32_to_bf16_rne,
+    check_bf16_decode, check_int2_decode, check_int4_decode, check_e2m1_table, check_pack_roundtrip,
+    check_int2_vs_fp64, check_int4_vs_fp64, check_mxfp4_vs_fp64, check_integer_x_exact,
+    check_single_segment_sequential, check_golden_order, check_threads_identical,
+    check_exp_accuracy, check_gelu_accuracy, check_rmsnorm_vs_fp64, check_fused_composition,
+    check_argmax_ties,
+]

@@ -1,0 +1,99 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check
+that the pins catch every one of them.  The real oracle is never modified."""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, text to replace, replacement, extra compiler flags, pin expected to fail)
+MUTANTS = [
+    ("tree_sequential",
+     "for (int p = 0; p < s; ++p) v[p] = v[p] + v[p + s];",
+     "if (s == 1) for (int p = 1; p < p2; ++p) v[0] = v[0] + v[p];",
+     (), P.check_golden_order),
+    ("tree_adjacent_pairs",
+     "for (int p = 0; p < s; ++p) v[p] = v[p] + v[p + s];",
+     "for (int p = 0; p < s; ++p) v[p] = v[2 * p] + v[2 * p + 1];",
+     (), P.check_golden_order),
+    ("int2_fields_swapped",
+     "static const int INT2_VALUE[4] = {0, 1, -2, -1};",
+     "static const int INT2_VALUE[4] = {0, 1, -1, -2};",
+     (), P.check_int2_decode),
+    ("int2_unsigned",
+     "static const int INT2_VALUE[4] = {0, 1, -2, -1};",
+     "static const int INT2_VALUE[4] = {-2, -1, 0, 1};",
+     (), P.check_int2_decode),
+    ("int4_bias_off_by_one",
+     "ORC_API int orc_int4_value(unsigned q) { return (int)(q & 15u) - 8; }",
+     "ORC_API int orc_int4_value(unsigned q) { return (int)(q & 15u) - 7; }",
+     (), P.check_int4_decode),
+    ("int4_group_scale_index",
+     "v[j] = orc_f16_to_f32(srow[j]) * t;",
+     "v[j] = orc_f16_to_f32(srow[j ^ 1]) * t;",
+     (), P.check_int4_vs_fp64),
+    ("mxfp4_nibble_order_in_fo",
+     "float c = orc_e2m1_value((k % 2 == 0) ? (b & 15u) : (b >> 4));",
+     "float c = orc_e2m1_value((k % 2 == 1) ? (b & 15u) : (b >> 4));",
+     (), P.check_mxfp4_vs_fp64),
+    ("mxfp4_scale_bias",
+     "return ldexpf(1.0f, (int)e - 127);",
+     "return ldexpf(1.0f, (int)e - 128);",
+     (), P.check_e2m1_table),
+    ("int2_dropped_last_code",
+     "for (int64_t k = 64 * (int64_t)j; k < 64 * (int64_t)j + 64; ++k) {\n            float c = (float)orc_int2_value",
+     "for (int64_t k = 64 * (int64_t)j; k < 64 * (int64_t)j + 63; ++k) {\n            float c = (float)orc_int2_value",
+     (), P.check_int2_vs_fp64),
+    ("f16_subnormal_exponent",
+     "v = ldexp((double)m, -24);",
+     "v = ldexp((double)m, -25);",
+     (), P.check_f16_decode_all),
+    ("f16_round_half_up",
+     "double r = nearbyint(q);            /* ties to even */",
+     "double r = floor(q + 0.5);",
+     (), P.check_f32_to_f16_rne),
+    ("exp_dropped_term",
+     "0x1.6c16c2p-10f, 0x1.a01a02p-13f};",
+     "0x0p+0f, 0x0p+0f};",
+     (), P.check_exp_accuracy),
+    ("gelu_constant",
+     "#define ORC_GELU_C 0x1.6e4e26p-5f",
+     "#define ORC_GELU_C 0x1.6e4e26p-4f",
+     (), P.check_gelu_accuracy),
+    ("rmsnorm_mean_over_k_minus_1",
+     "float ms = ss / (float)K;",
+     "float ms = ss / (float)(K - 1);",
+     (), P.check_rmsnorm_vs_fp64),
+    ("rmsnorm_residual_not_added",
+     "h_out[k] = orc_f64_to_f16((double)orc_f16_to_f32(x[k]) + (double)orc_f16_to_f32(r[k]));",
+     "h_out[k] = x[k];",
+     (), P.check_rmsnorm_vs_fp64),
+    ("argmax_last_max",
+     "if (y[m * N + n] > y[m * N + best]) best = n;",
+     "if (y[m * N + n] >= y[m * N + best]) best = n;",
+     (), P.check_argmax_ties),
+]
+
+
+@pytest.mark.parametrize("name,old,new,flags,check", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new, flags, check):
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation anchor for {name} not found"
+    src = tmp_path / f"oracle_{name}.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(obuild.build(str(src), str(tmp_path / f"lib_{name}.so"), flags, quiet=True))
+    with pytest.raises(AssertionError):
+        check(lib)
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """The same build route with no mutation passes the same pins."""
+    src = tmp_path / "oracle_copy.c"
+    src.write_text(open(SRC).read())
+    lib = oracle.load(obuild.build(str(src), str(tmp_path / "lib_copy.so"), (), quiet=True))
+    for check in {m[4] for m in MUTANTS}:
+        check(lib)
