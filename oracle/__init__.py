@@ -86,7 +86,11 @@ def _c(a, dtype):
 
 
 def default_threads():
-    return os.cpu_count() or 1
+    """Worker threads for the row-parallel oracle: OMP_NUM_THREADS if set,
+    else the CPU count, never more than 16."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+    return max(1, min(n, 16))
 
 
 # ---------------------------------------------------------------- matvecs --

@@ -1,0 +1,68 @@
+"""Build libqmv.so (the HIP library) in-tree for gfx950.
+
+    python -m skinny_gemm_qmv_amd.build          # or __graft_entry__.build()
+
+Flags:
+  --offload-arch=gfx950        MI355X only
+  -ffp-contract=off            HIP's default contracts a*b+c; the fixed order
+                               writes every fused multiply-add explicitly
+  -target-feature -packed-fp32-ops
+                               no v_pk_{add,mul,fma}_f32 in generated code
+  (no -ffast-math, no denormal flushing: the gfx950 default float mode keeps
+   fp32 and fp16 denormals)
+Set QMV_SAVE_TEMPS=1 to keep the generated gfx950 assembly under _build/.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libqmv.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["qmv_api.hip", "qmv_fo.hip"]
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include"),
+]
+
+
+def _compile(src):
+    os.makedirs(BUILD, exist_ok=True)
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if os.environ.get("QMV_SAVE_TEMPS"):
+        cmd += ["-save-temps=obj"]
+    res = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
+    # the host pass does not know the gfx950 feature flag: drop that one warning
+    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{err}")
+    return obj, err
+
+
+def build(verbose=False):
+    """Compile every HIP source for gfx950 and link libqmv.so; returns its path."""
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    for _, err in results:
+        if err.strip() and verbose:
+            sys.stderr.write(err + "\n")
+    objs = [o for o, _ in results]
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

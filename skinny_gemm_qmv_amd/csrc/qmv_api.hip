@@ -1,0 +1,160 @@
+// qmv_api.hip -- the extern "C" entry points declared in include/qmv.h:
+// argument validation, mode checks, workspace sizing and kernel dispatch.
+// No allocation, no host synchronisation, no global mutable state apart
+// from the per-thread text of the last HIP error.
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/qmv.h"
+#include "qmv_internal.hpp"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+qmv_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return QMV_OK;
+    snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return QMV_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dtype_size(qmv_dtype d) { return d == QMV_F32 ? 4 : 2; }
+
+bool valid_dtype(qmv_dtype d) { return d == QMV_F32 || d == QMV_F16 || d == QMV_BF16; }
+
+bool valid_mode(qmv_mode m) {
+    return m == QMV_MODE_FIXED || m == QMV_MODE_SPLITK || m == QMV_MODE_MFMA;
+}
+
+// Shape rules shared by every entry point: 1 <= M <= 256, N >= 1,
+// K a positive multiple of `kmul`, K <= QMV_MAX_K.
+bool valid_shape(int M, int N, int K, int kmul) {
+    return M >= 1 && M <= QMV_MAX_M && N >= 1 && K >= kmul && K % kmul == 0 && K <= QMV_MAX_K;
+}
+
+qmv_status check_matvec(const void *wq, const void *sc, const void *x, const void *y,
+                        qmv_dtype dt, int M, int N, int K, int kmul, qmv_mode mode) {
+    if (!wq || !sc || !x || !y) return QMV_ERR_INVALID_ARG;
+    if (!valid_shape(M, N, K, kmul) || !valid_dtype(dt) || !valid_mode(mode))
+        return QMV_ERR_INVALID_ARG;
+    if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(y, dtype_size(dt)))
+        return QMV_ERR_ALIGNMENT;
+    return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmv_abi_version(void) { return QMV_ABI_VERSION; }
+
+const char *qmv_status_string(qmv_status s) {
+    switch (s) {
+    case QMV_OK: return "ok";
+    case QMV_ERR_INVALID_ARG: return "invalid argument";
+    case QMV_ERR_ALIGNMENT: return "misaligned pointer";
+    case QMV_ERR_WORKSPACE: return "workspace missing or too small";
+    case QMV_ERR_UNSUPPORTED: return "mode not supported for this operation or shape";
+    case QMV_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+const char *qmv_last_hip_error(void) { return g_last_hip_error; }
+
+void qmv_fo_spec(int *segment_bytes, int *tree_kind, int *inner_step) {
+    if (segment_bytes) *segment_bytes = 16;
+    if (tree_kind) *tree_kind = 1;
+    if (inner_step) *inner_step = 1;
+}
+
+size_t qmv_workspace_size(qmv_op op, int M, int N, int K, qmv_mode mode) {
+    if (op == QMV_OP_INT2_ARGMAX) {
+        if (mode != QMV_MODE_FIXED || !valid_shape(M, N, K, 64)) return 0;
+        return qmv::argmax_workspace_bytes(M, N, K);
+    }
+    return 0;
+}
+
+qmv_status qmv_workspace_init(void *ws, size_t bytes, void *stream) {
+    if (bytes == 0) return QMV_OK;
+    if (!ws) return QMV_ERR_INVALID_ARG;
+    if (!aligned(ws, 256) || bytes % 4 != 0) return QMV_ERR_ALIGNMENT;
+    return hip_status(qmv::launch_fill_zero(ws, bytes, static_cast<hipStream_t>(stream)));
+}
+
+static qmv_status run_matvec(int fmt, const void *wq, const void *sc, const uint16_t *x, void *y,
+                             qmv_dtype dt, int M, int N, int K, qmv_mode mode, void *stream) {
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+    qmv::MatvecArgs a{fmt, wq, sc, x, y, (int)dt, M, N, K};
+    return hip_status(qmv::launch_fo_matvec(a, static_cast<hipStream_t>(stream)));
+}
+
+qmv_status qmv_int2(const uint32_t *wq, const uint16_t *scale, const uint16_t *x, void *y,
+                    qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
+                    size_t ws_bytes, void *stream) {
+    (void)workspace; (void)ws_bytes;
+    qmv_status s = check_matvec(wq, scale, x, y, y_dtype, M, N, K, 64, mode);
+    if (s != QMV_OK) return s;
+    if (mode == QMV_MODE_MFMA) return QMV_ERR_UNSUPPORTED;
+    return run_matvec(0, wq, scale, x, y, y_dtype, M, N, K, mode, stream);
+}
+
+qmv_status qmv_int4(const uint32_t *wq, const uint16_t *scales, const uint16_t *x, void *y,
+                    qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
+                    size_t ws_bytes, void *stream) {
+    (void)workspace; (void)ws_bytes;
+    qmv_status s = check_matvec(wq, scales, x, y, y_dtype, M, N, K, 32, mode);
+    if (s != QMV_OK) return s;
+    if (mode == QMV_MODE_MFMA) return QMV_ERR_UNSUPPORTED;
+    return run_matvec(1, wq, scales, x, y, y_dtype, M, N, K, mode, stream);
+}
+
+qmv_status qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_t *x, void *y,
+                     qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
+                     size_t ws_bytes, void *stream) {
+    (void)workspace; (void)ws_bytes;
+    qmv_status s = check_matvec(wq, e8m0, x, y, y_dtype, M, N, K, 32, mode);
+    if (s != QMV_OK) return s;
+    if (mode == QMV_MODE_MFMA) return QMV_ERR_UNSUPPORTED;
+    return run_matvec(2, wq, e8m0, x, y, y_dtype, M, N, K, mode, stream);
+}
+
+qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *residual,
+                                        uint16_t *residual_out, const uint16_t *gamma, float eps,
+                                        const uint32_t *wq_gate, const uint16_t *s_gate,
+                                        const uint32_t *wq_up, const uint16_t *s_up,
+                                        uint16_t *out, int M, int N, int K, qmv_mode mode,
+                                        void *workspace, size_t ws_bytes, void *stream) {
+    (void)workspace; (void)ws_bytes;
+    if (!x || !residual || !gamma || !wq_gate || !s_gate || !wq_up || !s_up || !out)
+        return QMV_ERR_INVALID_ARG;
+    if (!valid_shape(M, N, K, 64) || !valid_mode(mode) || !(eps >= 0.0f)) return QMV_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(wq_gate, 16) || !aligned(wq_up, 16) ||
+        !aligned(gamma, 2) || !aligned(out, 2) || (residual_out && !aligned(residual_out, 2)))
+        return QMV_ERR_ALIGNMENT;
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+    qmv::GateUpArgs a{x, residual, gamma, residual_out, eps, wq_gate, wq_up, s_gate, s_up, out, M, N, K};
+    return hip_status(qmv::launch_fo_gateup(a, static_cast<hipStream_t>(stream)));
+}
+
+qmv_status qmv_int2_argmax(const uint32_t *wq, const uint16_t *scale, const uint16_t *x,
+                           int32_t *idx, float *maxval, float *logits, int M, int N, int K,
+                           qmv_mode mode, void *workspace, size_t ws_bytes, void *stream) {
+    if (!wq || !scale || !x || !idx) return QMV_ERR_INVALID_ARG;
+    if (!valid_shape(M, N, K, 64) || !valid_mode(mode)) return QMV_ERR_INVALID_ARG;
+    if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(idx, 4) || (maxval && !aligned(maxval, 4)) ||
+        (logits && !aligned(logits, 4)))
+        return QMV_ERR_ALIGNMENT;
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+    const size_t need = qmv::argmax_workspace_bytes(M, N, K);
+    if (!workspace || ws_bytes < need) return QMV_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QMV_ERR_ALIGNMENT;
+    qmv::ArgmaxArgs a{wq, scale, x, idx, maxval, logits, M, N, K, workspace};
+    return hip_status(qmv::launch_fo_argmax(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

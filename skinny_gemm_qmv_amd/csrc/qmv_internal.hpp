@@ -1,0 +1,59 @@
+// qmv_internal.hpp -- host-side launch interface between the C ABI layer and
+// the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmv {
+
+// Per-row-group lane layout: RL lanes share one row, each lane owns the
+// segments j = q + RL*a (a < NI); NIP = lane-local tree width (power of two).
+struct LaneShape {
+    int RL, NI, NIP;
+};
+
+// Chooses the lane layout for a row of `nseg` 16-byte segments; returns
+// false if the row is longer than the compiled layouts allow.
+bool pick_shape(int nseg, LaneShape &s);
+
+struct MatvecArgs {
+    int fmt;            // 0 int2, 1 int4, 2 mxfp4
+    const void *wq;     // packed rows, 16 bytes per segment
+    const void *sc;     // int2: fp16 [N]; int4: fp16 [N][K/32]; mxfp4: uint8 [N][K/32]
+    const uint16_t *x;  // [M][K] fp16 or bf16
+    void *y;            // [M][N]
+    int y_dtype;
+    int M, N, K;
+};
+
+hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t stream);
+
+struct GateUpArgs {
+    const uint16_t *x, *residual, *gamma;
+    uint16_t *residual_out;
+    float eps;
+    const uint32_t *wq_gate, *wq_up;
+    const uint16_t *s_gate, *s_up;
+    uint16_t *out;
+    int M, N, K;
+};
+
+hipError_t launch_fo_gateup(const GateUpArgs &a, hipStream_t stream);
+
+struct ArgmaxArgs {
+    const uint32_t *wq;
+    const uint16_t *scale, *x;
+    int32_t *idx;
+    float *maxval, *logits;
+    int M, N, K;
+    void *ws;
+};
+
+size_t argmax_workspace_bytes(int M, int N, int K);
+hipError_t launch_fo_argmax(const ArgmaxArgs &a, hipStream_t stream);
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
+
+}  // namespace qmv

@@ -1,0 +1,127 @@
+"""The C ABI library on a host without a GPU: it loads, exports every entry
+point include/qmv.h declares, and its argument validation returns the
+documented status codes.  Every call below fails validation before any HIP
+call, so no GPU is touched."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+q = pytest.importorskip("skinny_gemm_qmv_amd")
+
+OK, INVALID, ALIGN, WS, UNSUP = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_\w+|qmm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu",
+                 "qmv_int2_argmax", "qmv_workspace_size", "qmv_workspace_init",
+                 "qmv_status_string", "qmv_last_hip_error", "qmv_abi_version", "qmv_fo_spec"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = C.CDLL(q.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_version_and_spec():
+    assert q.abi_version() == 1
+    assert q.fo_spec() == (16, 1, 1)
+    for s in range(6):
+        assert q._lib.qmv_status_string(s)
+
+
+P = C.c_void_p
+
+
+def _mv(fn, wq=16, sc=16, x=16, y=16, dt=0, M=1, N=64, K=64, mode=0, ws=None, wsb=0):
+    return fn(P(wq) if wq else None, P(sc) if sc else None, P(x) if x else None,
+              P(y) if y else None, dt, M, N, K, mode, P(ws) if ws else None, wsb, None)
+
+
+@pytest.mark.parametrize("name,kmul", [("qmv_int2", 64), ("qmv_int4", 32), ("qmm_mxfp4", 32)])
+def test_matvec_validation(name, kmul):
+    fn = getattr(q._lib, name)
+    assert _mv(fn, wq=0) == INVALID
+    assert _mv(fn, sc=0) == INVALID
+    assert _mv(fn, x=0) == INVALID
+    assert _mv(fn, y=0) == INVALID
+    assert _mv(fn, M=0) == INVALID
+    assert _mv(fn, M=257) == INVALID
+    assert _mv(fn, N=0) == INVALID
+    assert _mv(fn, K=kmul + kmul // 2) == INVALID
+    assert _mv(fn, K=0) == INVALID
+    assert _mv(fn, K=16384 + kmul) == INVALID
+    assert _mv(fn, dt=3) == INVALID
+    assert _mv(fn, mode=7) == INVALID
+    assert _mv(fn, wq=24) == ALIGN
+    assert _mv(fn, x=40) == ALIGN
+    assert _mv(fn, y=18) == ALIGN          # fp32 output needs 4-byte alignment
+    if name != "qmm_mxfp4":
+        assert _mv(fn, mode=2) == UNSUP       # matrix-core mode only for MXFP4
+    else:
+        assert _mv(fn, mode=2, M=16) == UNSUP  # MXFP4 matrix cores need M >= 32
+
+
+def test_gateup_validation():
+    fn = q._lib.qmv_int2_rmsnorm_gateup_gelu
+    args = [P(16)] * 4 + [C.c_float(1e-6)] + [P(16)] * 5
+
+    def call(args, M=1, N=64, K=64, mode=0):
+        return fn(*args, M, N, K, mode, None, 0, None)
+    a = list(args); a[0] = None
+    assert call(a) == INVALID
+    a = list(args); a[2] = None       # residual_out is optional: must not be the failure
+    a[5] = None
+    assert call(a) == INVALID
+    assert call(args, K=96) == INVALID
+    assert call(args, M=300) == INVALID
+    a = list(args); a[4] = C.c_float(-1.0)
+    assert call(a) == INVALID
+    a = list(args); a[0] = P(18)
+    assert call(a) == ALIGN
+    assert call(args, mode=2) == UNSUP    # matrix-core mode never applies to int2
+
+
+def test_argmax_validation():
+    fn = q._lib.qmv_int2_argmax
+
+    def call(wq=16, sc=16, x=16, idx=16, mv=None, lg=None, M=1, N=64, K=64, mode=0, ws=None, wsb=0):
+        return fn(P(wq) if wq else None, P(sc) if sc else None, P(x) if x else None,
+                  P(idx) if idx else None, P(mv) if mv else None, P(lg) if lg else None,
+                  M, N, K, mode, P(ws) if ws else None, wsb, None)
+    assert call(idx=0) == INVALID
+    assert call(K=100) == INVALID
+    assert call(mode=2) == UNSUP
+    assert call() == WS                  # no workspace
+    need = q.workspace_size("int2_argmax", 1, 64, 64)
+    assert need > 0
+    assert call(ws=256, wsb=need - 1) == WS
+    assert call(ws=128, wsb=need) == ALIGN
+    assert q.workspace_size("int2_argmax", 4, 262144, 1536) > q.workspace_size("int2_argmax", 1, 262144, 1536)
+    assert q.workspace_size("int2", 1, 64, 64) == 0
+
+
+def test_workspace_init_validation():
+    assert q._lib.qmv_workspace_init(None, 0, None) == OK
+    assert q._lib.qmv_workspace_init(None, 256, None) == INVALID
+    assert q._lib.qmv_workspace_init(P(128), 256, None) == ALIGN
+    assert q._lib.qmv_workspace_init(P(256), 6, None) == ALIGN
