@@ -33,13 +33,13 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    os.makedirs(BUILD, exist_ok=True)
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, build_dir=BUILD, defines=()):
+    os.makedirs(build_dir, exist_ok=True)
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *["-D" + d for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     if os.environ.get("QMV_SAVE_TEMPS"):
         cmd += ["-save-temps=obj"]
-    res = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
+    res = subprocess.run(cmd, capture_output=True, text=True, cwd=build_dir)
     # the host pass does not know the gfx950 feature flag: drop that one warning
     err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
@@ -47,21 +47,23 @@ def _compile(src):
     return obj, err
 
 
-def build(verbose=False):
-    """Compile every HIP source for gfx950 and link libqmv.so; returns its path."""
+def build(verbose=False, out=LIB, defines=(), build_dir=BUILD):
+    """Compile every HIP source for gfx950 and link libqmv.so; returns its path.
+    `defines` (NAME=VALUE strings) and `out` build a variant elsewhere, e.g. to
+    compare launch shapes (QMV_BLOCK, QMV_MAX_GRID, QMV_RING, QMV_XREG_BUDGET)."""
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
     for _, err in results:
         if err.strip() and verbose:
             sys.stderr.write(err + "\n")
     objs = [o for o, _ in results]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + " ".join(cmd) + "\n" + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/qmv.h"
+#include "qmv.h"
 #include "qmv_internal.hpp"
 
 namespace {
@@ -35,11 +35,18 @@ bool valid_shape(int M, int N, int K, int kmul) {
     return M >= 1 && M <= QMV_MAX_M && N >= 1 && K >= kmul && K % kmul == 0 && K <= QMV_MAX_K;
 }
 
+// Kernels address each weight / scale tensor with 32-bit byte offsets
+// (buffer loads), so one tensor must stay below 4 GiB.
+bool fits_32bit(int N, int K, int codes_per_byte) {
+    return (uint64_t)N * (uint64_t)(K / codes_per_byte) < (1ull << 32) - (1ull << 16);
+}
+
 qmv_status check_matvec(const void *wq, const void *sc, const void *x, const void *y,
                         qmv_dtype dt, int M, int N, int K, int kmul, qmv_mode mode) {
     if (!wq || !sc || !x || !y) return QMV_ERR_INVALID_ARG;
     if (!valid_shape(M, N, K, kmul) || !valid_dtype(dt) || !valid_mode(mode))
         return QMV_ERR_INVALID_ARG;
+    if (!fits_32bit(N, K, kmul == 64 ? 4 : 2)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(y, dtype_size(dt)))
         return QMV_ERR_ALIGNMENT;
     return QMV_OK;
@@ -133,6 +140,7 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *resid
     if (!x || !residual || !gamma || !wq_gate || !s_gate || !wq_up || !s_up || !out)
         return QMV_ERR_INVALID_ARG;
     if (!valid_shape(M, N, K, 64) || !valid_mode(mode) || !(eps >= 0.0f)) return QMV_ERR_INVALID_ARG;
+    if (!fits_32bit(N, K, 4)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(wq_gate, 16) || !aligned(wq_up, 16) ||
         !aligned(gamma, 2) || !aligned(out, 2) || (residual_out && !aligned(residual_out, 2)))
         return QMV_ERR_ALIGNMENT;
@@ -146,6 +154,7 @@ qmv_status qmv_int2_argmax(const uint32_t *wq, const uint16_t *scale, const uint
                            qmv_mode mode, void *workspace, size_t ws_bytes, void *stream) {
     if (!wq || !scale || !x || !idx) return QMV_ERR_INVALID_ARG;
     if (!valid_shape(M, N, K, 64) || !valid_mode(mode)) return QMV_ERR_INVALID_ARG;
+    if (!fits_32bit(N, K, 4)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(idx, 4) || (maxval && !aligned(maxval, 4)) ||
         (logits && !aligned(logits, 4)))
         return QMV_ERR_ALIGNMENT;

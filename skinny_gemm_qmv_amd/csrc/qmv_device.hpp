@@ -46,36 +46,66 @@ __device__ __forceinline__ h2_t fma_h2(h2_t a, float mul, float add) {
     return __builtin_elementwise_fma(a, m, c);
 }
 
+// Hide a value from constant folding (no instruction is emitted).  gfx9 VOP3
+// encodings cannot carry literal constants, so the decode masks live in
+// SGPRs and the fp16 magic in a VGPR; v_and_or_b32 then does mask-and-insert
+// in one instruction.
+__device__ __forceinline__ uint32_t in_sgpr(uint32_t v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // fp16 1024.0 in both halves: OR-ing a field into the low mantissa bits of
 // this pattern gives the fp16 value 1024 + field * 2^(bit position).
 constexpr uint32_t kMagic1024 = 0x64006400u;
+
+struct DecodeConsts {
+    uint32_t magic;                // VGPR
+    uint32_t m2[5];                // int2 field masks, fields i and i+8 at bits 2i / 2i+16
+    uint32_t m4lo, m4hi, xor2;     // int4 masks, int2 bias flip
+    __device__ __forceinline__ DecodeConsts() {
+        magic = in_vgpr(kMagic1024);
+        m2[0] = in_sgpr(0x00030003u);
+        m2[1] = in_sgpr(0x000C000Cu);
+        m2[2] = in_sgpr(0x00300030u);
+        m2[3] = in_sgpr(0x00C000C0u);
+        m2[4] = in_sgpr(0x03000300u);
+        m4lo = in_sgpr(0x000F000Fu);
+        m4hi = in_sgpr(0x00F000F0u);
+        xor2 = in_sgpr(0xAAAAAAAAu);
+    }
+};
 
 // int2: 16 two's-complement 2-bit fields of one word -> 8 packed fp16 pairs,
 // pair i = (code i, code i+8).  XOR with 0b10 in every field maps the field
 // f to f^2 = value + 2 in 0..3; the field is placed in an fp16 mantissa
 // (1024 + 4^i (value+2)) and one exact packed fma scales by 4^-i and removes
 // the bias: (1024 + 4^i b) 4^-i - (1024 4^-i + 2) = b - 2.
-__device__ __forceinline__ void int2_decode_word(uint32_t w, h2_t (&c)[8]) {
-    const uint32_t u = w ^ 0xAAAAAAAAu;
+__device__ __forceinline__ void int2_decode_word(uint32_t w, const DecodeConsts &k, h2_t (&c)[8]) {
+    const uint32_t u = w ^ k.xor2;
     const uint32_t v = u >> 10;  // fields 5..7 and 13..15 to bits 0..5 / 16..21
-    c[0] = fma_h2(u2h2((u & 0x00030003u) | kMagic1024), 1.0f, -1026.0f);
-    c[1] = fma_h2(u2h2((u & 0x000C000Cu) | kMagic1024), 0.25f, -258.0f);
-    c[2] = fma_h2(u2h2((u & 0x00300030u) | kMagic1024), 0.0625f, -66.0f);
-    c[3] = fma_h2(u2h2((u & 0x00C000C0u) | kMagic1024), 0.015625f, -18.0f);
-    c[4] = fma_h2(u2h2((u & 0x03000300u) | kMagic1024), 0.00390625f, -6.0f);
-    c[5] = fma_h2(u2h2((v & 0x00030003u) | kMagic1024), 1.0f, -1026.0f);
-    c[6] = fma_h2(u2h2((v & 0x000C000Cu) | kMagic1024), 0.25f, -258.0f);
-    c[7] = fma_h2(u2h2((v & 0x00300030u) | kMagic1024), 0.0625f, -66.0f);
+    c[0] = fma_h2(u2h2((u & k.m2[0]) | k.magic), 1.0f, -1026.0f);
+    c[1] = fma_h2(u2h2((u & k.m2[1]) | k.magic), 0.25f, -258.0f);
+    c[2] = fma_h2(u2h2((u & k.m2[2]) | k.magic), 0.0625f, -66.0f);
+    c[3] = fma_h2(u2h2((u & k.m2[3]) | k.magic), 0.015625f, -18.0f);
+    c[4] = fma_h2(u2h2((u & k.m2[4]) | k.magic), 0.00390625f, -6.0f);
+    c[5] = fma_h2(u2h2((v & k.m2[0]) | k.magic), 1.0f, -1026.0f);
+    c[6] = fma_h2(u2h2((v & k.m2[1]) | k.magic), 0.25f, -258.0f);
+    c[7] = fma_h2(u2h2((v & k.m2[2]) | k.magic), 0.0625f, -66.0f);
 }
 
 // int4: 8 nibbles q of one word -> 4 packed fp16 pairs of q - 8,
 // pair i = (code i, code i+4).
-__device__ __forceinline__ void int4_decode_word(uint32_t w, h2_t (&c)[4]) {
+__device__ __forceinline__ void int4_decode_word(uint32_t w, const DecodeConsts &k, h2_t (&c)[4]) {
     const uint32_t v = w >> 8;
-    c[0] = fma_h2(u2h2((w & 0x000F000Fu) | kMagic1024), 1.0f, -1032.0f);
-    c[1] = fma_h2(u2h2((w & 0x00F000F0u) | kMagic1024), 0.0625f, -72.0f);
-    c[2] = fma_h2(u2h2((v & 0x000F000Fu) | kMagic1024), 1.0f, -1032.0f);
-    c[3] = fma_h2(u2h2((v & 0x00F000F0u) | kMagic1024), 0.0625f, -72.0f);
+    c[0] = fma_h2(u2h2((w & k.m4lo) | k.magic), 1.0f, -1032.0f);
+    c[1] = fma_h2(u2h2((w & k.m4hi) | k.magic), 0.0625f, -72.0f);
+    c[2] = fma_h2(u2h2((v & k.m4lo) | k.magic), 1.0f, -1032.0f);
+    c[3] = fma_h2(u2h2((v & k.m4hi) | k.magic), 0.0625f, -72.0f);
 }
 
 // E8M0 block scale as an fp32 value: 2^(E-127), exact for E in 0..254
@@ -84,64 +114,91 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return e == 0u ? u2f(0x00400000u) : (e == 255u ? u2f(0x7FC00000u) : u2f(e << 23));
 }
 
-// Inner step of one 16-byte segment for MC activation columns:
-//   t[m] = t[m] (+) value_k * x[m][k]   for k ascending over the segment.
-// XF(m, v) returns 8 consecutive activation values (16 bytes) of column m at
-// segment offset 8v.
-template <int F, int MC, class XF>
-__device__ __forceinline__ void segment_sum(const u4_t &w, XF &&xf, float (&t)[MC]) {
-    if constexpr (F == FMT_INT2) {
+// Inner step for the NS segments a lane holds in one row group, for MC
+// activation columns:
+//   t[a][m] = t[a][m] (+) value_k * x[m][k]   for k ascending over segment a.
+// The NS x MC chains are independent; they are advanced together one code at
+// a time so consecutive fused multiply-adds never depend on each other, while
+// each chain still adds its products in code order.  XF(a, m, v) returns 8
+// consecutive activation values (16 bytes) of column m at offset 8v of the
+// lane's segment a.
+template <int F, int NS, int MC, class XF>
+__device__ __forceinline__ void segment_sums(const u4_t (&w)[NS], const DecodeConsts &kc, XF &&xf,
+                                             float (&t)[NS][MC]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            h2_t c[8];
-            int2_decode_word(w[q], c);
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (F == FMT_INT2) {
+            h2_t c[NS][8];
 #pragma unroll
-            for (int m = 0; m < MC; ++m) {
-                const u4_t xa = xf(m, 2 * q), xb = xf(m, 2 * q + 1);
-                const uint32_t xs[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+            for (int a = 0; a < NS; ++a) int2_decode_word(w[a][q], kc, c[a]);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const _Float16 cv = (i < 8) ? c[i].x : c[i - 8].y;
-                    const h2_t xp = u2h2(xs[i >> 1]);
-                    const _Float16 xv = (i & 1) ? xp.y : xp.x;
-                    t[m] = __builtin_fmaf((float)cv, (float)xv, t[m]);  // exact product
-                }
-            }
-        }
-    } else if constexpr (F == FMT_INT4) {
+            for (int half = 0; half < 2; ++half) {  // codes 16q + 8half .. +7
+                u4_t xa[NS][MC];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            h2_t c[4];
-            int4_decode_word(w[q], c);
+                for (int a = 0; a < NS; ++a)
 #pragma unroll
-            for (int m = 0; m < MC; ++m) {
-                const u4_t xa = xf(m, q);
+                    for (int m = 0; m < MC; ++m) xa[a][m] = xf(a, m, 2 * q + half);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const _Float16 cv = (i < 4) ? c[i].x : c[i - 4].y;
-                    const h2_t xp = u2h2(xa[i >> 1]);
-                    const _Float16 xv = (i & 1) ? xp.y : xp.x;
-                    t[m] = __builtin_fmaf((float)cv, (float)xv, t[m]);
+#pragma unroll
+                    for (int a = 0; a < NS; ++a) {
+                        const _Float16 cv = half ? c[a][i].y : c[a][i].x;
+#pragma unroll
+                        for (int m = 0; m < MC; ++m) {
+                            const h2_t xp = u2h2(xa[a][m][i >> 1]);
+                            const _Float16 xv = (i & 1) ? xp.y : xp.x;
+                            t[a][m] = __builtin_fmaf((float)cv, (float)xv, t[a][m]);  // exact product
+                        }
+                    }
                 }
             }
-        }
-    } else {  // MXFP4: byte b of word q holds elements 8q+2b (low) and 8q+2b+1 (high)
+        } else if constexpr (F == FMT_INT4) {
+            h2_t c[NS][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            f2_t c[4];
-            c[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 0);
-            c[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 1);
-            c[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 2);
-            c[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 3);
+            for (int a = 0; a < NS; ++a) int4_decode_word(w[a][q], kc, c[a]);
+            u4_t xa[NS][MC];
 #pragma unroll
-            for (int m = 0; m < MC; ++m) {
-                const u4_t xa = xf(m, q);
+            for (int a = 0; a < NS; ++a)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float cv = (i & 1) ? c[i >> 1].y : c[i >> 1].x;
-                    const uint32_t xp = xa[i >> 1];
-                    const float xv = (i & 1) ? u2f(xp & 0xFFFF0000u) : u2f(xp << 16);
-                    t[m] = __builtin_fmaf(cv, xv, t[m]);
+                for (int m = 0; m < MC; ++m) xa[a][m] = xf(a, m, q);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int a = 0; a < NS; ++a) {
+                    const _Float16 cv = (i < 4) ? c[a][i].x : c[a][i - 4].y;
+#pragma unroll
+                    for (int m = 0; m < MC; ++m) {
+                        const h2_t xp = u2h2(xa[a][m][i >> 1]);
+                        const _Float16 xv = (i & 1) ? xp.y : xp.x;
+                        t[a][m] = __builtin_fmaf((float)cv, (float)xv, t[a][m]);
+                    }
+                }
+            }
+        } else {  // MXFP4: byte b of word q holds elements 8q+2b (low) and 8q+2b+1 (high)
+            f2_t c[NS][4];
+#pragma unroll
+            for (int a = 0; a < NS; ++a) {
+                c[a][0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[a][q], 1.0f, 0);
+                c[a][1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[a][q], 1.0f, 1);
+                c[a][2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[a][q], 1.0f, 2);
+                c[a][3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[a][q], 1.0f, 3);
+            }
+            u4_t xa[NS][MC];
+#pragma unroll
+            for (int a = 0; a < NS; ++a)
+#pragma unroll
+                for (int m = 0; m < MC; ++m) xa[a][m] = xf(a, m, q);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int a = 0; a < NS; ++a) {
+                    const float cv = (i & 1) ? c[a][i >> 1].y : c[a][i >> 1].x;
+#pragma unroll
+                    for (int m = 0; m < MC; ++m) {
+                        const uint32_t xp = xa[a][m][i >> 1];
+                        const float xv = (i & 1) ? u2f(xp & 0xFFFF0000u) : u2f(xp << 16);
+                        t[a][m] = __builtin_fmaf(cv, xv, t[a][m]);
+                    }
                 }
             }
         }

@@ -19,9 +19,19 @@
 
 namespace qmv {
 
-constexpr int kBlock = 256;  // 4 waves of 64
+// Launch shape; the macros let a build explore other shapes.
+#ifndef QMV_BLOCK
+#define QMV_BLOCK 256
+#endif
+#ifndef QMV_MAX_GRID
+#define QMV_MAX_GRID 1024
+#endif
+#ifndef QMV_XREG_BUDGET
+#define QMV_XREG_BUDGET 96
+#endif
+constexpr int kBlock = QMV_BLOCK;  // waves of 64 lanes per workgroup
 constexpr int kWaves = kBlock / 64;
-constexpr int kMaxGrid = 2048;
+constexpr int kMaxGrid = QMV_MAX_GRID;
 
 bool pick_shape(int nseg, LaneShape &s) {
     if (nseg <= 0) return false;
@@ -46,129 +56,260 @@ static inline int pow2_ceil(int n) {
 
 // ---------------------------------------------------------------------------
 // Activation staging: rows m0 .. m0+MC-1 of x[M][K] -> LDS xs[MC][K]
-// (zeros for rows beyond M).  16-byte vector copies.
+// (zeros for rows beyond M), 16-byte vectors.  Split in two so that the
+// global loads of x are issued before the weight prefetch: vector loads
+// retire in issue order, so waiting for x issued after the weights would
+// also wait for the weights.  Up to kXpt vectors per thread go through
+// registers; any remainder is copied after the prefetch.
+constexpr int kXpt = 4;
+
 template <int MC>
-__device__ __forceinline__ void stage_x(const uint16_t *__restrict__ x, uint16_t *xs, int M, int K,
-                                        int m0) {
-    const int per_row = K / 8;
-    for (int e = threadIdx.x; e < MC * per_row; e += blockDim.x) {
-        const int m = e / per_row, kk = e - m * per_row;
-        u4_t v = {0u, 0u, 0u, 0u};
-        if (m0 + m < M) v = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * K + 8 * kk);
-        *reinterpret_cast<u4_t *>(xs + (size_t)m * K + 8 * kk) = v;
+struct XStage {
+    u4_t v[kXpt];
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int M, int K, int m0) {
+        const int per_row = K / 8;
+#pragma unroll
+        for (int r = 0; r < kXpt; ++r) {
+            const int e = threadIdx.x + r * blockDim.x;
+            v[r] = u4_t{0u, 0u, 0u, 0u};
+            if (e < MC * per_row) {
+                const int m = MC == 1 ? 0 : e / per_row, kk = e - m * per_row;
+                if (m0 + m < M) v[r] = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * K + 8 * kk);
+            }
+        }
     }
+    __device__ __forceinline__ void store(const uint16_t *__restrict__ x, uint16_t *xs, int M, int K,
+                                          int m0) {
+        const int per_row = K / 8;
+#pragma unroll
+        for (int r = 0; r < kXpt; ++r) {
+            const int e = threadIdx.x + r * blockDim.x;
+            if (e < MC * per_row) *reinterpret_cast<u4_t *>(xs + 8 * e) = v[r];
+        }
+        for (int e = threadIdx.x + kXpt * blockDim.x; e < MC * per_row; e += blockDim.x) {
+            const int m = MC == 1 ? 0 : e / per_row, kk = e - m * per_row;
+            u4_t w = {0u, 0u, 0u, 0u};
+            if (m0 + m < M) w = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * K + 8 * kk);
+            *reinterpret_cast<u4_t *>(xs + (size_t)m * K + 8 * kk) = w;
+        }
+    }
+};
+
+// Ring depth: how many row groups a wave keeps in flight besides the one it
+// is computing.  One measured fastest on MI355X for every format: deeper
+// rings cost registers (fewer resident waves) without adding bandwidth.
+template <int NI, int NMAT>
+constexpr int ring_depth() {
+#ifdef QMV_RING
+    return QMV_RING;
+#else
+    return 1;
+#endif
 }
 
-// ---------------------------------------------------------------------------
-// The FO row engine.  NMAT weight matrices (1, or 2 for gate/up) share the
-// activation chunk.  For every row group the wave produces, in lane q == 0 of
-// each RL-lane group, the reduced totals tot[mat][m] (before the int2 row
-// scale) and hands them to the epilogue.
-template <int F, int RL, int NI, int NIP, int MC, bool XREG, int NMAT, class Epi>
-__device__ __forceinline__ void fo_rows(const uint8_t *const (&wq)[NMAT],
-                                        const void *const (&sc)[NMAT], const uint16_t *xs, int N,
-                                        int K, Epi &epi) {
-    constexpr int CODES = SegCodes<F>::v;
-    constexpr int XV = CODES / 8;  // 16-byte activation vectors per segment per column
-    constexpr int RPG = 64 / RL;   // rows per wave per iteration
-    const int nseg = K / CODES;
-    int P2 = 1;
-    while (P2 < nseg) P2 <<= 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int q = lane % RL, rsub = lane / RL;
-    const size_t row_bytes = (size_t)nseg * 16;
-    const int total_rg = (N + RPG - 1) / RPG;
-    const int nwaves = gridDim.x * kWaves;
+// Raw loaded bits only: converting a scale in the load routine would make
+// the wave wait for that load right there.
+template <int F, int NI, int NMAT>
+struct RowSlot {
+    u4_t w[NMAT][NI];
+    uint32_t seg[NMAT][NI];  // int4 / MXFP4 segment scale bits (fp16 / E8M0)
+    uint32_t rs[NMAT];       // int2 row scale bits (fp16)
+};
 
-    u4_t xr[XREG ? NI : 1][XREG ? MC : 1][XREG ? XV : 1];
-    if constexpr (XREG) {
+template <int F>
+__device__ __forceinline__ float seg_scale(uint32_t bits) {
+    if constexpr (F == FMT_INT4) return half_bits_to_f32((uint16_t)bits);
+    else return e8m0_to_f32(bits);
+}
+
+// The FO row engine.  NMAT weight matrices (1, or 2 for gate/up) share the
+// activation chunk.  Each wave walks its row groups rg = first, first+stride,
+// ... through a ring of D load slots: the weights (and scales) of the next D
+// row groups are always in flight while one is being computed.  prefetch()
+// issues the first D loads and is called before the activations are staged,
+// so that staging overlaps the first weight fetches.  For every row group,
+// lane q == 0 of each RL-lane group hands the reduced totals tot[mat][m]
+// (before the int2 row scale) and the row scales rs[mat] to the epilogue.
+template <int F, int RL, int NI, int NIP, int MC, bool XREG, int NMAT, int D>
+struct FoEngine {
+    static constexpr int CODES = SegCodes<F>::v;
+    static constexpr int XV = CODES / 8;  // 16-byte activation vectors per segment per column
+    static constexpr int RPG = 64 / RL;   // rows per wave per row group
+
+    int N, K, nseg, P2, q, rsub, total_rg, stride, first;
+    uint32_t row_bytes;
+    // Buffer descriptors (SGPRs) for the packed weights and their scales.
+    // Raw buffer loads take a 32-bit per-lane offset and return zero for any
+    // offset past the end of the buffer, so rows past N (a partial last row
+    // group, or row groups past the end) need no clamps or branches.
+    __amdgpu_buffer_rsrc_t rw[NMAT], rsc[NMAT];
+    uint32_t woff, soff;        // offsets of the next row group to load
+    uint32_t wstep, sstep;      // bytes between consecutive row groups of a wave
+    RowSlot<F, NI, NMAT> slot[D];
+
+    static constexpr int kNT = 2;  // non-temporal: the weights are read once
+
+    __device__ __forceinline__ FoEngine(const uint8_t *const (&wq)[NMAT], const void *const (&sc)[NMAT],
+                                        int N_, int K_)
+        : N(N_), K(K_) {
+        nseg = K / CODES;
+        P2 = 1;
+        while (P2 < nseg) P2 <<= 1;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        q = lane % RL;
+        rsub = lane / RL;
+        row_bytes = (uint32_t)nseg * 16u;
+        total_rg = (N + RPG - 1) / RPG;
+        stride = gridDim.x * kWaves;
+        first = blockIdx.x * kWaves + wave;
+        // bytes of scale data per row
+        const uint32_t srow = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u * nseg : (uint32_t)nseg);
+        const uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);  // bytes per scale
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t) {
+            rw[t] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wq[t]), 0,
+                                                     (uint32_t)N * row_bytes, 0x00020000);
+            rsc[t] = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(sc[t]), 0,
+                                                      (uint32_t)N * srow, 0x00020000);
+        }
+        const uint32_t n0 = (uint32_t)first * RPG + rsub;
+        woff = n0 * row_bytes + (uint32_t)q * 16u;
+        soff = n0 * srow + (F == FMT_INT2 ? 0u : (uint32_t)q * ssz);
+        wstep = (uint32_t)stride * RPG * row_bytes;
+        sstep = (uint32_t)stride * RPG * srow;
+    }
+
+    // Issue the loads of the next row group in this wave's sequence into `sl`.
+    // Loads are unconditional (the compiler can then count outstanding loads
+    // exactly); segments past a row's end read the next row's bytes, which
+    // are never used.
+    __device__ __forceinline__ void load(RowSlot<F, NI, NMAT> &sl) {
+        constexpr uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t) {
+            if constexpr (F == FMT_INT2)
+                sl.rs[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff, 0, 0);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                sl.w[t][i] = __builtin_bit_cast(
+                    u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[t], woff + (uint32_t)(i * RL * 16), 0, kNT));
+                if constexpr (F == FMT_INT4)
+                    sl.seg[t][i] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff + (uint32_t)(i * RL) * ssz, 0, 0);
+                else if constexpr (F == FMT_MXFP4)
+                    sl.seg[t][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc[t], soff + (uint32_t)(i * RL) * ssz, 0, 0);
+            }
+        }
+        woff += wstep;
+        soff += sstep;
+    }
+
+    __device__ __forceinline__ void prefetch() {
+#pragma unroll
+        for (int d = 0; d < D; ++d) load(slot[d]);
+    }
+
+    template <class Epi>
+    __device__ __forceinline__ void run(const uint16_t *xs, Epi &epi) {
+        const DecodeConsts kc;
+        // x slice of this lane: segments q + RL*i (zeros past the row end)
+        u4_t xr[XREG ? NI : 1][XREG ? MC : 1][XREG ? XV : 1];
+        if constexpr (XREG) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int j = q + RL * i;
+#pragma unroll
+                for (int m = 0; m < MC; ++m)
+#pragma unroll
+                    for (int v = 0; v < XV; ++v)
+                        xr[i][m][v] = (j < nseg) ? *reinterpret_cast<const u4_t *>(
+                                                       xs + (size_t)m * K + j * CODES + 8 * v)
+                                                 : u4_t{0u, 0u, 0u, 0u};
+            }
+        }
+        int xoff[NI];  // LDS offset of each segment's activations (clamped)
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int j = q + RL * i;
-#pragma unroll
-            for (int m = 0; m < MC; ++m)
-#pragma unroll
-                for (int v = 0; v < XV; ++v)
-                    xr[i][m][v] = (j < nseg)
-                                      ? *reinterpret_cast<const u4_t *>(xs + (size_t)m * K + j * CODES + 8 * v)
-                                      : u4_t{0u, 0u, 0u, 0u};
+            xoff[i] = (j < nseg ? j : nseg - 1) * CODES;
         }
-    }
-
-    for (int rg = blockIdx.x * kWaves + wave; rg < total_rg; rg += nwaves) {
-        const int n = rg * RPG + rsub;
-        const int nl = n < N ? n : N - 1;
-        u4_t w[NMAT][NI];
-        float segscale[NMAT][NI];
+        for (int base = first; base < total_rg; base += D * stride) {
 #pragma unroll
-        for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int j = q + RL * i;
-                w[t][i] = u4_t{0u, 0u, 0u, 0u};
-                segscale[t][i] = 0.0f;
-                if (j < nseg) {
-                    w[t][i] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u4_t *>(wq[t] + (size_t)nl * row_bytes + (size_t)j * 16));
-                    if constexpr (F == FMT_INT4)
-                        segscale[t][i] = half_bits_to_f32(
-                            reinterpret_cast<const uint16_t *>(sc[t])[(size_t)nl * nseg + j]);
-                    else if constexpr (F == FMT_MXFP4)
-                        segscale[t][i] =
-                            e8m0_to_f32(reinterpret_cast<const uint8_t *>(sc[t])[(size_t)nl * nseg + j]);
-                }
-            }
-        float tot[NMAT][MC];
-#pragma unroll
-        for (int t = 0; t < NMAT; ++t) {
-            float v[MC][NIP];
-#pragma unroll
-            for (int m = 0; m < MC; ++m)
-#pragma unroll
-                for (int a = 0; a < NIP; ++a) v[m][a] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int j = q + RL * i;
-                if (j < nseg) {
-                    float acc[MC];
-#pragma unroll
-                    for (int m = 0; m < MC; ++m) acc[m] = 0.0f;
+            for (int d = 0; d < D; ++d) {
+                const int rg = base + d * stride;
+                // take this slot's data and refill the slot with the row group
+                // D steps ahead before computing, so the wave always has D row
+                // groups in flight (the copy costs no instructions: the
+                // compiler renames registers)
+                const RowSlot<F, NI, NMAT> cur = slot[d];
+                load(slot[d]);
+                if (rg < total_rg) {  // uniform across the wave
                     if constexpr (XREG) {
-                        segment_sum<F, MC>(w[t][i], [&](int m, int vv) { return xr[i][m][vv]; }, acc);
-                    } else {
-                        const uint16_t *xseg = xs + (size_t)j * CODES;
-                        segment_sum<F, MC>(
-                            w[t][i],
-                            [&](int m, int vv) {
-                                return *reinterpret_cast<const u4_t *>(xseg + (size_t)m * K + 8 * vv);
-                            },
-                            acc);
-                    }
+                        // keep the register copy of x opaque to loop-invariant
+                        // code motion (it would hoist fp16->fp32 conversions
+                        // and double the registers x occupies)
 #pragma unroll
-                    for (int m = 0; m < MC; ++m) {
-                        if constexpr (F == FMT_INT2) v[m][i] = acc[m];
-                        else if constexpr (F == FMT_INT4) v[m][i] = segscale[t][i] * acc[m];
-                        else v[m][i] = acc[m] * segscale[t][i];
+                        for (int i = 0; i < NI; ++i)
+#pragma unroll
+                            for (int m = 0; m < MC; ++m)
+#pragma unroll
+                                for (int v = 0; v < XV; ++v) asm volatile("" : "+v"(xr[i][m][v]));
                     }
+                    float tot[NMAT][MC];
+#pragma unroll
+                    for (int t = 0; t < NMAT; ++t) {
+                        float acc[NI][MC];
+#pragma unroll
+                        for (int i = 0; i < NI; ++i)
+#pragma unroll
+                            for (int m = 0; m < MC; ++m) acc[i][m] = 0.0f;
+                        if constexpr (XREG) {
+                            segment_sums<F, NI, MC>(cur.w[t], kc,
+                                                    [&](int a, int m, int vv) { return xr[a][m][vv]; }, acc);
+                        } else {
+                            segment_sums<F, NI, MC>(
+                                cur.w[t], kc,
+                                [&](int a, int m, int vv) {
+                                    return *reinterpret_cast<const u4_t *>(xs + (size_t)m * K + xoff[a] + 8 * vv);
+                                },
+                                acc);
+                        }
+#pragma unroll
+                        for (int m = 0; m < MC; ++m) {
+                            float v[NIP];
+#pragma unroll
+                            for (int a = 0; a < NIP; ++a) {
+                                float val = 0.0f;
+                                if (a < NI) {
+                                    if constexpr (F == FMT_INT2) val = acc[a][m];
+                                    else if constexpr (F == FMT_INT4) val = seg_scale<F>(cur.seg[t][a]) * acc[a][m];
+                                    else val = acc[a][m] * seg_scale<F>(cur.seg[t][a]);
+                                    // segments past the row end are the tree's +0 padding
+                                    val = (q + RL * a < nseg) ? val : 0.0f;
+                                }
+                                v[a] = val;
+                            }
+                            tot[t][m] = fo_tree<RL, NIP>(v, P2);
+                        }
+                    }
+                    float rs[NMAT];
+#pragma unroll
+                    for (int t = 0; t < NMAT; ++t) rs[t] = half_bits_to_f32((uint16_t)cur.rs[t]);
+                    epi(rg * RPG + rsub, q, tot, rs);
                 }
             }
-#pragma unroll
-            for (int m = 0; m < MC; ++m) tot[t][m] = fo_tree<RL, NIP>(v[m], P2);
         }
-        epi(n, nl, q, tot);
     }
-}
+};
 
 // ---------------------------------------------------------------------------
 // Plain matvec / skinny GEMM.
 template <int F, int MC>
 struct StoreEpi {
-    const uint16_t *row_scale;  // int2 only
     void *y;
     int y_dtype, M, N, m0;
-    __device__ __forceinline__ void operator()(int n, int nl, int q, const float (&tot)[1][MC]) {
-        float s = 1.0f;
-        if constexpr (F == FMT_INT2) s = half_bits_to_f32(row_scale[nl]);
+    __device__ __forceinline__ void operator()(int n, int q, const float (&tot)[1][MC],
+                                               const float (&rs)[1]) {
+        const float s = rs[0];
         if (q != 0 || n >= N) return;
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
@@ -188,12 +329,16 @@ __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict_
                                                       int y_dtype, int M, int N, int K) {
     extern __shared__ __align__(16) uint16_t xs[];
     const int m0 = blockIdx.y * MC;
-    stage_x<MC>(x, xs, M, K, m0);
-    __syncthreads();
-    StoreEpi<F, MC> epi{reinterpret_cast<const uint16_t *>(sc), y, y_dtype, M, N, m0};
     const uint8_t *const w1[1] = {wq};
     const void *const s1[1] = {sc};
-    fo_rows<F, RL, NI, NIP, MC, XREG, 1>(w1, s1, xs, N, K, epi);
+    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>()> eng(w1, s1, N, K);
+    XStage<MC> xst;
+    xst.load(x, M, K, m0);
+    eng.prefetch();
+    xst.store(x, xs, M, K, m0);
+    __syncthreads();
+    StoreEpi<F, MC> epi{y, y_dtype, M, N, m0};
+    eng.run(xs, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -266,12 +411,12 @@ __device__ void rmsnorm_prologue(const uint16_t *__restrict__ x, const uint16_t 
 
 template <int MC>
 struct GateUpEpi {
-    const uint16_t *s_gate, *s_up;
     uint16_t *out;
     int M, N, m0;
-    __device__ __forceinline__ void operator()(int n, int nl, int q, const float (&tot)[2][MC]) {
-        const float sg = half_bits_to_f32(s_gate[nl]);
-        const float su = half_bits_to_f32(s_up[nl]);
+    __device__ __forceinline__ void operator()(int n, int q, const float (&tot)[2][MC],
+                                               const float (&rs)[2]) {
+        const float sg = rs[0];
+        const float su = rs[1];
         if (q != 0 || n >= N) return;
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
@@ -297,27 +442,34 @@ __global__ __launch_bounds__(kBlock) void k_fo_gateup(
     uint16_t *xs = smem;  // [MC][K]: h, then overwritten in place by the normalised xn
     float *inv_s = reinterpret_cast<float *>(smem + (size_t)MC * K);
     const int m0 = blockIdx.y * MC;
-    rmsnorm_prologue<MC>(x, residual, gamma, residual_out, eps, M, K, m0, xs, xs, inv_s);
-    GateUpEpi<MC> epi{s_gate, s_up, out, M, N, m0};
     const uint8_t *const w2[2] = {reinterpret_cast<const uint8_t *>(wq_gate),
                                   reinterpret_cast<const uint8_t *>(wq_up)};
     const void *const s2[2] = {s_gate, s_up};
-    fo_rows<FMT_INT2, RL, NI, NIP, MC, XREG, 2>(w2, s2, xs, N, K, epi);
+    FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 2, ring_depth<NI, 2>()> eng(w2, s2, N, K);
+    eng.prefetch();
+    rmsnorm_prologue<MC>(x, residual, gamma, residual_out, eps, M, K, m0, xs, xs, inv_s);
+    GateUpEpi<MC> epi{out, M, N, m0};
+    eng.run(xs, epi);
 }
 
 // ---------------------------------------------------------------------------
-// int2 lm_head + argmax.  Each lane keeps the best key of the rows it
-// produced; the workgroup reduces them, writes one key per activation row to
-// the workspace, and the last workgroup to finish (completion counter) reduces
-// all keys, writes idx / maxval and resets the counter to zero.
+// int2 lm_head + argmax, one dispatch ("The parked levers": argmax stages 1
+// and 2 merged, first-max tie-break kept).  Each lane keeps the best key of
+// the rows it produced; the workgroup reduces them and folds its best key per
+// activation row into a 64-bit key in the workspace with an agent-scope
+// atomic max (order-independent, so the result is exact).  Only after those
+// atomics have returned does the workgroup take a ticket from the completion
+// counter; the workgroup that takes the last ticket reads each key with an
+// atomic exchange (which also resets it to zero), writes idx / maxval and
+// resets the counter, leaving the workspace zeroed for the next call.
 template <int MC>
 struct ArgmaxEpi {
-    const uint16_t *row_scale;
     float *logits;
     int M, N, m0;
     uint64_t best[MC];
-    __device__ __forceinline__ void operator()(int n, int nl, int q, const float (&tot)[1][MC]) {
-        const float s = half_bits_to_f32(row_scale[nl]);
+    __device__ __forceinline__ void operator()(int n, int q, const float (&tot)[1][MC],
+                                               const float (&rs)[1]) {
+        const float s = rs[0];
         if (q != 0 || n >= N) return;
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
@@ -343,19 +495,24 @@ __global__ __launch_bounds__(kBlock) void k_fo_argmax(const uint32_t *__restrict
                                                       const uint16_t *__restrict__ scale,
                                                       const uint16_t *__restrict__ x, int32_t *idx,
                                                       float *maxval, float *logits, int M, int N,
-                                                      int K, uint64_t *partial, uint32_t *counter) {
+                                                      int K, uint64_t *keys, uint32_t *counter) {
     extern __shared__ __align__(16) uint16_t xs[];
     __shared__ uint64_t wbest[kWaves][MC];
+    __shared__ uint64_t returned[MC];
     __shared__ int is_last;
     const int m0 = blockIdx.y * MC;
-    stage_x<MC>(x, xs, M, K, m0);
-    __syncthreads();
-    ArgmaxEpi<MC> epi{scale, logits, M, N, m0, {}};
-#pragma unroll
-    for (int m = 0; m < MC; ++m) epi.best[m] = 0ull;
     const uint8_t *const w1[1] = {reinterpret_cast<const uint8_t *>(wq)};
     const void *const s1[1] = {scale};
-    fo_rows<FMT_INT2, RL, NI, NIP, MC, XREG, 1>(w1, s1, xs, N, K, epi);
+    FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>()> eng(w1, s1, N, K);
+    XStage<MC> xst;
+    xst.load(x, M, K, m0);
+    eng.prefetch();
+    xst.store(x, xs, M, K, m0);
+    __syncthreads();
+    ArgmaxEpi<MC> epi{logits, M, N, m0, {}};
+#pragma unroll
+    for (int m = 0; m < MC; ++m) epi.best[m] = 0ull;
+    eng.run(xs, epi);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -364,38 +521,31 @@ __global__ __launch_bounds__(kBlock) void k_fo_argmax(const uint32_t *__restrict
         if (lane == 0) wbest[wave][m] = b;
     }
     __syncthreads();
-    uint64_t *slot = partial + ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * MC;
-    if (threadIdx.x < MC) {
+    if (threadIdx.x < MC && m0 + (int)threadIdx.x < M) {
         uint64_t b = 0;
         for (int w = 0; w < kWaves; ++w) b = wbest[w][threadIdx.x] > b ? wbest[w][threadIdx.x] : b;
-        __hip_atomic_store(&slot[threadIdx.x], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the returned value is consumed (written to LDS) before the barrier,
+        // so every key update of this workgroup has been performed before the
+        // ticket below is taken
+        returned[threadIdx.x] = __hip_atomic_fetch_max(&keys[m0 + threadIdx.x], b, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t ticket = __hip_atomic_fetch_add(&counter[blockIdx.y], 1u, __ATOMIC_ACQ_REL,
+        const uint32_t ticket = __hip_atomic_fetch_add(&counter[blockIdx.y], 1u, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
         is_last = (ticket == gridDim.x - 1) ? 1 : 0;
     }
     __syncthreads();
     if (!is_last) return;
-    __threadfence();
-    const uint64_t *chunk = partial + (size_t)blockIdx.y * gridDim.x * MC;
-    for (int m = wave; m < MC; m += kWaves) {
-        uint64_t b = 0;
-        for (int g = lane; g < (int)gridDim.x; g += 64) {
-            const uint64_t v = __hip_atomic_load(&chunk[(size_t)g * MC + m], __ATOMIC_RELAXED,
+    if (threadIdx.x < MC && m0 + (int)threadIdx.x < M) {
+        const uint64_t b = __hip_atomic_exchange(&keys[m0 + threadIdx.x], 0ull, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-            b = v > b ? v : b;
-        }
-        b = wave_max_u64(b);
-        if (lane == 0 && m0 + m < M) {
-            int n;
-            float yv;
-            argmax_key_decode(b, n, yv);
-            idx[m0 + m] = n;
-            if (maxval != nullptr) maxval[m0 + m] = yv;
-        }
+        int n;
+        float yv;
+        argmax_key_decode(b, n, yv);
+        idx[m0 + threadIdx.x] = n;
+        if (maxval != nullptr) maxval[m0 + threadIdx.x] = yv;
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&counter[blockIdx.y], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -410,11 +560,23 @@ __global__ void k_fill_zero(uint32_t *p, size_t words) {
 // ---------------------------------------------------------------------------
 // Host launchers.
 
-static int grid_for(int N, int RL) {
+// Workgroups for N rows: enough waves that each has about `depth` row
+// groups (its ring filled once), but no more than can be resident on the
+// device at once (occupancy x CUs), so every workgroup starts in the first
+// wave of the launch and none waits for a free CU.
+template <class Kern>
+static int grid_for(Kern kernel, size_t lds, int N, int RL, int depth) {
     const int rpg = 64 / RL;
     const long total_rg = ((long)N + rpg - 1) / rpg;
-    long g = (total_rg + kWaves - 1) / kWaves;
-    if (g > kMaxGrid) g = kMaxGrid;
+    long g = (total_rg + (long)kWaves * depth - 1) / ((long)kWaves * depth);
+    int dev = 0, cus = 256, occ = 1;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kBlock, lds) != hipSuccess || occ < 1)
+        occ = 1;
+    const long cap = (long)occ * cus;
+    if (g > cap) g = cap;
+    if (kMaxGrid > 0 && g > kMaxGrid) g = kMaxGrid;
     if (g < 1) g = 1;
     return (int)g;
 }
@@ -425,7 +587,7 @@ constexpr int kMcWide = 4;
 
 // Registers a lane spends on its activation slice when MC = 1 (16-byte
 // vectors x 4 VGPRs); above this budget the slice is read from LDS instead.
-constexpr int kXregBudget = 96;
+constexpr int kXregBudget = QMV_XREG_BUDGET;
 
 // Dynamic LDS per workgroup is kept within 64 KB; chunks of kMcWide
 // activation rows are used when they fit, single rows otherwise.
@@ -441,20 +603,25 @@ constexpr bool xreg_fits() {
 
 template <int F, int RL, int NI, int NIP>
 static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
-    const int grid = grid_for(a.N, RL);
+    constexpr int D = ring_depth<NI, 1>();
     const uint8_t *wq = reinterpret_cast<const uint8_t *>(a.wq);
     if (a.M == 1) {
         constexpr bool xreg = xreg_fits<F, NI>();
-        hipLaunchKernelGGL((k_fo_matvec<F, RL, NI, NIP, 1, xreg>), dim3(grid, 1), dim3(kBlock),
-                           (size_t)a.K * 2, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M, a.N, a.K);
+        auto k = k_fo_matvec<F, RL, NI, NIP, 1, xreg>;
+        const size_t lds = (size_t)a.K * 2;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), 1), dim3(kBlock), lds, st, wq, a.sc,
+                           a.x, a.y, a.y_dtype, a.M, a.N, a.K);
     } else if (wide_fits(a.K, 1)) {
+        auto k = k_fo_matvec<F, RL, NI, NIP, kMcWide, false>;
         const size_t lds = (size_t)kMcWide * a.K * 2;
         const int gy = (a.M + kMcWide - 1) / kMcWide;
-        hipLaunchKernelGGL((k_fo_matvec<F, RL, NI, NIP, kMcWide, false>), dim3(grid, gy),
-                           dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M, a.N, a.K);
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), gy), dim3(kBlock), lds, st, wq, a.sc,
+                           a.x, a.y, a.y_dtype, a.M, a.N, a.K);
     } else {
-        hipLaunchKernelGGL((k_fo_matvec<F, RL, NI, NIP, 1, false>), dim3(grid, a.M), dim3(kBlock),
-                           (size_t)a.K * 2, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M, a.N, a.K);
+        auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
+        const size_t lds = (size_t)a.K * 2;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), a.M), dim3(kBlock), lds, st, wq, a.sc,
+                           a.x, a.y, a.y_dtype, a.M, a.N, a.K);
     }
     return hipGetLastError();
 }
@@ -491,23 +658,27 @@ hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t st) {
 
 template <int RL, int NI, int NIP>
 static hipError_t gu_shape(const GateUpArgs &a, hipStream_t st) {
-    const int grid = grid_for(a.N, RL);
+    constexpr int D = ring_depth<NI, 2>();
     if (a.M == 1 || !wide_fits(a.K, 1)) {
         const size_t lds = (size_t)a.K * 2 + 64;
-        if (a.M == 1)
-            hipLaunchKernelGGL((k_fo_gateup<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>), dim3(grid, 1),
-                               dim3(kBlock), lds, st, a.x, a.residual, a.residual_out, a.gamma, a.eps,
-                               a.wq_gate, a.s_gate, a.wq_up, a.s_up, a.out, a.M, a.N, a.K);
-        else
-            hipLaunchKernelGGL((k_fo_gateup<RL, NI, NIP, 1, false>), dim3(grid, a.M), dim3(kBlock), lds,
-                               st, a.x, a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate,
-                               a.s_gate, a.wq_up, a.s_up, a.out, a.M, a.N, a.K);
+        if (a.M == 1) {
+            auto k = k_fo_gateup<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>;
+            hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), 1), dim3(kBlock), lds, st, a.x,
+                               a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
+                               a.s_up, a.out, a.M, a.N, a.K);
+        } else {
+            auto k = k_fo_gateup<RL, NI, NIP, 1, false>;
+            hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), a.M), dim3(kBlock), lds, st, a.x,
+                               a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
+                               a.s_up, a.out, a.M, a.N, a.K);
+        }
     } else {
+        auto k = k_fo_gateup<RL, NI, NIP, kMcWide, false>;
         const size_t lds = (size_t)kMcWide * a.K * 2 + 64 * kMcWide;
         const int gy = (a.M + kMcWide - 1) / kMcWide;
-        hipLaunchKernelGGL((k_fo_gateup<RL, NI, NIP, kMcWide, false>), dim3(grid, gy), dim3(kBlock),
-                           lds, st, a.x, a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate,
-                           a.s_gate, a.wq_up, a.s_up, a.out, a.M, a.N, a.K);
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), gy), dim3(kBlock), lds, st, a.x,
+                           a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
+                           a.s_up, a.out, a.M, a.N, a.K);
     }
     return hipGetLastError();
 }
@@ -529,31 +700,31 @@ constexpr size_t kCounterBytes = 1024;  // one 32-bit completion counter per chu
 size_t argmax_workspace_bytes(int M, int N, int K) {
     LaneShape sh;
     if (M < 1 || N < 1 || !pick_shape(K / 64, sh)) return 0;
-    int mc, gy;
-    argmax_chunks(M, K, mc, gy);
-    const size_t partial = (size_t)gy * grid_for(N, sh.RL) * mc * sizeof(uint64_t);
-    return kCounterBytes + ((partial + 255) / 256) * 256;  // counters, then partial keys
+    return kCounterBytes + (((size_t)M * sizeof(uint64_t) + 255) / 256) * 256;  // counters, keys
 }
 
 template <int RL, int NI, int NIP>
 static hipError_t am_shape(const ArgmaxArgs &a, hipStream_t st) {
-    const int grid = grid_for(a.N, RL);
+    constexpr int D = ring_depth<NI, 1>();
     uint32_t *counter = reinterpret_cast<uint32_t *>(a.ws);
-    uint64_t *partial = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(a.ws) + kCounterBytes);
+    uint64_t *keys = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(a.ws) + kCounterBytes);
     int mc, gy;
     argmax_chunks(a.M, a.K, mc, gy);
     if (a.M == 1) {
-        hipLaunchKernelGGL((k_fo_argmax<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>), dim3(grid, 1),
-                           dim3(kBlock), (size_t)a.K * 2, st, a.wq, a.scale, a.x, a.idx, a.maxval,
-                           a.logits, a.M, a.N, a.K, partial, counter);
+        auto k = k_fo_argmax<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>;
+        const size_t lds = (size_t)a.K * 2;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), 1), dim3(kBlock), lds, st, a.wq,
+                           a.scale, a.x, a.idx, a.maxval, a.logits, a.M, a.N, a.K, keys, counter);
     } else if (mc == 1) {
-        hipLaunchKernelGGL((k_fo_argmax<RL, NI, NIP, 1, false>), dim3(grid, gy), dim3(kBlock),
-                           (size_t)a.K * 2, st, a.wq, a.scale, a.x, a.idx, a.maxval, a.logits, a.M,
-                           a.N, a.K, partial, counter);
+        auto k = k_fo_argmax<RL, NI, NIP, 1, false>;
+        const size_t lds = (size_t)a.K * 2;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), gy), dim3(kBlock), lds, st, a.wq,
+                           a.scale, a.x, a.idx, a.maxval, a.logits, a.M, a.N, a.K, keys, counter);
     } else {
-        hipLaunchKernelGGL((k_fo_argmax<RL, NI, NIP, kMcWide, false>), dim3(grid, gy), dim3(kBlock),
-                           (size_t)kMcWide * a.K * 2, st, a.wq, a.scale, a.x, a.idx, a.maxval,
-                           a.logits, a.M, a.N, a.K, partial, counter);
+        auto k = k_fo_argmax<RL, NI, NIP, kMcWide, false>;
+        const size_t lds = (size_t)kMcWide * a.K * 2;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), gy), dim3(kBlock), lds, st, a.wq,
+                           a.scale, a.x, a.idx, a.maxval, a.logits, a.M, a.N, a.K, keys, counter);
     }
     return hipGetLastError();
 }
