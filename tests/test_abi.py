@@ -116,7 +116,9 @@ def test_argmax_validation():
     assert need > 0
     assert call(ws=256, wsb=need - 1) == WS
     assert call(ws=128, wsb=need) == ALIGN
-    assert q.workspace_size("int2_argmax", 4, 262144, 1536) > q.workspace_size("int2_argmax", 1, 262144, 1536)
+    # completion counters plus one 64-bit key per activation row
+    assert q.workspace_size("int2_argmax", 256, 262144, 1536) >= 1024 + 8 * 256
+    assert q.workspace_size("int2_argmax", 256, 64, 64) > q.workspace_size("int2_argmax", 1, 64, 64)
     assert q.workspace_size("int2", 1, 64, 64) == 0
 
 
