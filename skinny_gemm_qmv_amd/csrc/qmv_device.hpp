@@ -205,6 +205,133 @@ __device__ __forceinline__ void segment_sums(const u4_t (&w)[NS], const DecodeCo
     }
 }
 
+// v_fma_mix_f32 with two fp16 sources taken from halves of packed
+// registers (AH / BH = 1 selects the high half) and an fp32 addend:
+// acc = acc (+) a*b with one rounding.  fp16 x fp16 products are exact in
+// fp32, so this is the fixed-order step.  Written as an instruction so that
+// the compiler keeps the operands in fp16 (it would otherwise widen a shared
+// operand once and hold the fp32 copies in registers).
+template <int AH, int BH>
+__device__ __forceinline__ void mix_mac(float &acc, uint32_t a2, uint32_t b2) {
+    if constexpr (AH == 0 && BH == 0)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+    else if constexpr (AH == 1 && BH == 0)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+    else if constexpr (AH == 0 && BH == 1)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+}
+
+// Inner step for one segment of R rows (the same segment index of R
+// different rows) and MC activation columns read from LDS:
+//   t[r][m] = t[r][m] (+) value[r]_k * x[m][k]   for k ascending over the segment.
+// xs + xo is the segment's first activation of column 0; column m is K
+// elements further on.  The segment is walked in steps of 8 codes; each
+// step reads one 16-byte activation vector per column and uses every value
+// for all R rows.  The LDS offset is re-derived through an opaque copy at
+// every step so the reads stay next to their use (hoisting them makes the
+// compiler hold a whole segment of activations for every column).
+template <int F, int R, int MC>
+__device__ __forceinline__ void segment_sums_rows(const u4_t (&w)[R], const DecodeConsts &kc,
+                                                  const uint16_t *xs, int xo, int K,
+                                                  float (&t)[R][MC]) {
+    constexpr int STEPS = SegCodes<F>::v / 8;
+    // `dep` carries a value of the previous step into the opaque offset, so
+    // a step's reads can be issued once the previous step has started but
+    // not earlier (an opaque copy alone may be scheduled anywhere before).
+    float dep = 0.0f;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        int o = xo + 8 * st;
+        asm volatile("" : "+v"(o) : "v"(dep));
+        u4_t xa[MC];
+#pragma unroll
+        for (int m = 0; m < MC; ++m) xa[m] = *reinterpret_cast<const u4_t *>(xs + m * K + o);
+        if constexpr (F == FMT_INT2) {
+            // word st/2; fp16 pair i of a word = (code i, code i+8)
+            h2_t c[R][8];
+#pragma unroll
+            for (int r = 0; r < R; ++r) int2_decode_word(w[r][st >> 1], kc, c[r]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int m = 0; m < MC; ++m)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t cp = __builtin_bit_cast(uint32_t, c[r][i]);
+                        const uint32_t xp = xa[m][i >> 1];
+                        if (st & 1) {
+                            if (i & 1) mix_mac<1, 1>(t[r][m], cp, xp);
+                            else mix_mac<1, 0>(t[r][m], cp, xp);
+                        } else {
+                            if (i & 1) mix_mac<0, 1>(t[r][m], cp, xp);
+                            else mix_mac<0, 0>(t[r][m], cp, xp);
+                        }
+                    }
+                if (i == 0) dep = t[0][0];
+            }
+        } else if constexpr (F == FMT_INT4) {
+            // fp16 pair p of a word = (code p, code p+4)
+            h2_t c[R][4];
+#pragma unroll
+            for (int r = 0; r < R; ++r) int4_decode_word(w[r][st], kc, c[r]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int m = 0; m < MC; ++m)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t cp = __builtin_bit_cast(uint32_t, c[r][i & 3]);
+                        const uint32_t xp = xa[m][i >> 1];
+                        if (i >= 4) {
+                            if (i & 1) mix_mac<1, 1>(t[r][m], cp, xp);
+                            else mix_mac<1, 0>(t[r][m], cp, xp);
+                        } else {
+                            if (i & 1) mix_mac<0, 1>(t[r][m], cp, xp);
+                            else mix_mac<0, 0>(t[r][m], cp, xp);
+                        }
+                    }
+                if (i == 0) dep = t[0][0];
+            }
+        } else {  // MXFP4: byte b of word st holds elements 8st+2b (low) and 8st+2b+1 (high)
+            // the word goes through an opaque copy too: converted early, the
+            // codes of every step would be live at once
+            f2_t c[R][4];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                uint32_t wv = w[r][st];
+                asm volatile("" : "+v"(wv) : "v"(dep));
+                c[r][0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv, 1.0f, 0);
+                c[r][1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv, 1.0f, 1);
+                c[r][2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv, 1.0f, 2);
+                c[r][3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv, 1.0f, 3);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int m = 0; m < MC; ++m) {
+                    const uint32_t xp = xa[m][i >> 1];
+                    const float xv = (i & 1) ? u2f(xp & 0xFFFF0000u) : u2f(xp << 16);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const float cv = (i & 1) ? c[r][i >> 1].y : c[r][i >> 1].x;
+                        t[r][m] = __builtin_fmaf(cv, xv, t[r][m]);
+                    }
+                }
+                if (i == 0) dep = t[0][0];
+            }
+        }
+        // every chain finishes this step before any starts the next: left
+        // free, the compiler runs chains one after another and then needs the
+        // activations of all steps at once
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MC; ++m) asm volatile("" : "+v"(t[r][m]));
+    }
+}
+
 // Fixed-order tree over the segment values of one row.  Lane q of a group
 // of RL lanes holds the segments j = q + RL*a in v[a] (+0 beyond the row's
 // segment count).  The halving tree over P2 entries

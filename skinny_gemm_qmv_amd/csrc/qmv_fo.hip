@@ -107,13 +107,23 @@ constexpr int ring_depth() {
 #endif
 }
 
+// Rows blocked per unit: several activation columns read from LDS use each
+// activation value for QMV_ROWS rows; one column keeps the register copy.
+#ifndef QMV_ROWS
+#define QMV_ROWS 2
+#endif
+template <int MC, bool XREG>
+constexpr int rows_block() {
+    return (MC > 1 && !XREG) ? QMV_ROWS : 1;
+}
+
 // Raw loaded bits only: converting a scale in the load routine would make
-// the wave wait for that load right there.
-template <int F, int NI, int NMAT>
+// the wave wait for that load right there.  A slot holds R row groups.
+template <int F, int NI, int NMAT, int R>
 struct RowSlot {
-    u4_t w[NMAT][NI];
-    uint32_t seg[NMAT][NI];  // int4 / MXFP4 segment scale bits (fp16 / E8M0)
-    uint32_t rs[NMAT];       // int2 row scale bits (fp16)
+    u4_t w[NMAT][R][NI];
+    uint32_t seg[NMAT][R][NI];  // int4 / MXFP4 segment scale bits (fp16 / E8M0)
+    uint32_t rs[NMAT][R];       // int2 row scale bits (fp16)
 };
 
 template <int F>
@@ -123,29 +133,33 @@ __device__ __forceinline__ float seg_scale(uint32_t bits) {
 }
 
 // The FO row engine.  NMAT weight matrices (1, or 2 for gate/up) share the
-// activation chunk.  Each wave walks its row groups rg = first, first+stride,
-// ... through a ring of D load slots: the weights (and scales) of the next D
-// row groups are always in flight while one is being computed.  prefetch()
+// activation chunk.  A wave walks units u = first, first+stride, ...; a unit
+// is R adjacent row groups of RPG rows each.  Loads go through a ring of D
+// slots: the next D units are in flight while one is computed.  prefetch()
 // issues the first D loads and is called before the activations are staged,
-// so that staging overlaps the first weight fetches.  For every row group,
-// lane q == 0 of each RL-lane group hands the reduced totals tot[mat][m]
-// (before the int2 row scale) and the row scales rs[mat] to the epilogue.
-template <int F, int RL, int NI, int NIP, int MC, bool XREG, int NMAT, int D>
+// so staging overlaps the first weight fetches.  For every row group, lane
+// q == 0 of each RL-lane group hands the reduced totals tot[mat][m] (before
+// the int2 row scale) and the row scales rs[mat] to the epilogue.
+//
+// R > 1 (used with several activation columns read from LDS): every
+// activation value read (and widened) is used for R rows, which divides the
+// LDS traffic and conversion work per multiply-add by R.
+template <int F, int RL, int NI, int NIP, int MC, bool XREG, int NMAT, int D, int R>
 struct FoEngine {
     static constexpr int CODES = SegCodes<F>::v;
     static constexpr int XV = CODES / 8;  // 16-byte activation vectors per segment per column
     static constexpr int RPG = 64 / RL;   // rows per wave per row group
 
-    int N, K, nseg, P2, q, rsub, total_rg, stride, first;
-    uint32_t row_bytes;
+    int N, K, nseg, P2, q, rsub, total_units, stride, first;
+    uint32_t row_bytes, srow;
     // Buffer descriptors (SGPRs) for the packed weights and their scales.
     // Raw buffer loads take a 32-bit per-lane offset and return zero for any
     // offset past the end of the buffer, so rows past N (a partial last row
-    // group, or row groups past the end) need no clamps or branches.
+    // group, or units past the end) need no clamps or branches.
     __amdgpu_buffer_rsrc_t rw[NMAT], rsc[NMAT];
-    uint32_t woff, soff;        // offsets of the next row group to load
-    uint32_t wstep, sstep;      // bytes between consecutive row groups of a wave
-    RowSlot<F, NI, NMAT> slot[D];
+    uint32_t woff, soff;        // offsets of the next unit to load
+    uint32_t wstep, sstep;      // bytes between consecutive units of a wave
+    RowSlot<F, NI, NMAT, R> slot[D];
 
     static constexpr int kNT = 2;  // non-temporal: the weights are read once
 
@@ -159,11 +173,12 @@ struct FoEngine {
         q = lane % RL;
         rsub = lane / RL;
         row_bytes = (uint32_t)nseg * 16u;
-        total_rg = (N + RPG - 1) / RPG;
+        const int total_rg = (N + RPG - 1) / RPG;
+        total_units = (total_rg + R - 1) / R;
         stride = gridDim.x * kWaves;
         first = blockIdx.x * kWaves + wave;
         // bytes of scale data per row
-        const uint32_t srow = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u * nseg : (uint32_t)nseg);
+        srow = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u * nseg : (uint32_t)nseg);
         const uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);  // bytes per scale
 #pragma unroll
         for (int t = 0; t < NMAT; ++t) {
@@ -172,33 +187,38 @@ struct FoEngine {
             rsc[t] = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(sc[t]), 0,
                                                       (uint32_t)N * srow, 0x00020000);
         }
-        const uint32_t n0 = (uint32_t)first * RPG + rsub;
+        const uint32_t n0 = (uint32_t)first * R * RPG + rsub;
         woff = n0 * row_bytes + (uint32_t)q * 16u;
         soff = n0 * srow + (F == FMT_INT2 ? 0u : (uint32_t)q * ssz);
-        wstep = (uint32_t)stride * RPG * row_bytes;
-        sstep = (uint32_t)stride * RPG * srow;
+        wstep = (uint32_t)stride * R * RPG * row_bytes;
+        sstep = (uint32_t)stride * R * RPG * srow;
     }
 
-    // Issue the loads of the next row group in this wave's sequence into `sl`.
+    // Issue the loads of the next unit in this wave's sequence into `sl`.
     // Loads are unconditional (the compiler can then count outstanding loads
     // exactly); segments past a row's end read the next row's bytes, which
     // are never used.
-    __device__ __forceinline__ void load(RowSlot<F, NI, NMAT> &sl) {
+    __device__ __forceinline__ void load(RowSlot<F, NI, NMAT, R> &sl) {
         constexpr uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);
 #pragma unroll
-        for (int t = 0; t < NMAT; ++t) {
-            if constexpr (F == FMT_INT2)
-                sl.rs[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff, 0, 0);
+        for (int t = 0; t < NMAT; ++t)
 #pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                sl.w[t][i] = __builtin_bit_cast(
-                    u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[t], woff + (uint32_t)(i * RL * 16), 0, kNT));
-                if constexpr (F == FMT_INT4)
-                    sl.seg[t][i] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff + (uint32_t)(i * RL) * ssz, 0, 0);
-                else if constexpr (F == FMT_MXFP4)
-                    sl.seg[t][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc[t], soff + (uint32_t)(i * RL) * ssz, 0, 0);
+            for (int r = 0; r < R; ++r) {
+                const uint32_t wo = woff + (uint32_t)r * RPG * row_bytes;
+                const uint32_t so = soff + (uint32_t)r * RPG * srow;
+                if constexpr (F == FMT_INT2) sl.rs[t][r] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], so, 0, 0);
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    sl.w[t][r][i] = __builtin_bit_cast(
+                        u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[t], wo + (uint32_t)(i * RL * 16), 0, kNT));
+                    if constexpr (F == FMT_INT4)
+                        sl.seg[t][r][i] =
+                            __builtin_amdgcn_raw_buffer_load_b16(rsc[t], so + (uint32_t)(i * RL) * ssz, 0, 0);
+                    else if constexpr (F == FMT_MXFP4)
+                        sl.seg[t][r][i] =
+                            __builtin_amdgcn_raw_buffer_load_b8(rsc[t], so + (uint32_t)(i * RL) * ssz, 0, 0);
+                }
             }
-        }
         woff += wstep;
         soff += sstep;
     }
@@ -206,6 +226,24 @@ struct FoEngine {
     __device__ __forceinline__ void prefetch() {
 #pragma unroll
         for (int d = 0; d < D; ++d) load(slot[d]);
+    }
+
+    // Scale the segment sums and pad past the row end (+0), then reduce.
+    __device__ __forceinline__ float finish(const float (&seg)[NI], const uint32_t (&sbits)[NI]) const {
+        float v[NIP];
+#pragma unroll
+        for (int a = 0; a < NIP; ++a) {
+            float val = 0.0f;
+            if (a < NI) {
+                if constexpr (F == FMT_INT2) val = seg[a];
+                else if constexpr (F == FMT_INT4) val = seg_scale<F>(sbits[a]) * seg[a];
+                else val = seg[a] * seg_scale<F>(sbits[a]);
+                // segments past the row end are the tree's +0 padding
+                val = (q + RL * a < nseg) ? val : 0.0f;
+            }
+            v[a] = val;
+        }
+        return fo_tree<RL, NIP>(v, P2);
     }
 
     template <class Epi>
@@ -232,17 +270,18 @@ struct FoEngine {
             const int j = q + RL * i;
             xoff[i] = (j < nseg ? j : nseg - 1) * CODES;
         }
-        for (int base = first; base < total_rg; base += D * stride) {
+        for (int base = first; base < total_units; base += D * stride) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                const int rg = base + d * stride;
-                // take this slot's data and refill the slot with the row group
-                // D steps ahead before computing, so the wave always has D row
-                // groups in flight (the copy costs no instructions: the
-                // compiler renames registers)
-                const RowSlot<F, NI, NMAT> cur = slot[d];
-                load(slot[d]);
-                if (rg < total_rg) {  // uniform across the wave
+                const int u = base + d * stride;
+                // With one activation column the wave refills a slot before
+                // computing it (D units always in flight); with several read
+                // from LDS the kernel is bound by arithmetic and two live slots
+                // would cost the registers that set its occupancy.
+                constexpr bool kRefillFirst = XREG || MC == 1;
+                const RowSlot<F, NI, NMAT, R> cur = slot[d];
+                if constexpr (kRefillFirst) load(slot[d]);
+                if (u < total_units) {  // uniform across the wave
                     if constexpr (XREG) {
                         // keep the register copy of x opaque to loop-invariant
                         // code motion (it would hoist fp16->fp32 conversions
@@ -253,49 +292,74 @@ struct FoEngine {
                             for (int m = 0; m < MC; ++m)
 #pragma unroll
                                 for (int v = 0; v < XV; ++v) asm volatile("" : "+v"(xr[i][m][v]));
+                    } else {
+                        // the LDS copy of x never changes, so the compiler
+                        // would hoist every read (and a widening of it) out of
+                        // the row loop and run out of registers; opaque
+                        // offsets keep the reads here
+#pragma unroll
+                        for (int i = 0; i < NI; ++i) asm volatile("" : "+v"(xoff[i]));
                     }
-                    float tot[NMAT][MC];
+                    float tot[R][NMAT][MC];
 #pragma unroll
                     for (int t = 0; t < NMAT; ++t) {
-                        float acc[NI][MC];
+                        float acc[R][MC][NI];
+                        if constexpr (R == 1 && MC == 1) {
+                            // one row, one column: the lane's segments are the
+                            // independent chains, advanced together
+                            float a1[NI][1];
 #pragma unroll
-                        for (int i = 0; i < NI; ++i)
+                            for (int i = 0; i < NI; ++i) a1[i][0] = 0.0f;
+                            if constexpr (XREG)
+                                segment_sums<F, NI, 1>(cur.w[t][0], kc,
+                                                       [&](int a, int m, int vv) { return xr[a][m][vv]; }, a1);
+                            else
+                                segment_sums<F, NI, 1>(
+                                    cur.w[t][0], kc,
+                                    [&](int a, int m, int vv) {
+                                        return *reinterpret_cast<const u4_t *>(xs + xoff[a] + 8 * vv);
+                                    },
+                                    a1);
 #pragma unroll
-                            for (int m = 0; m < MC; ++m) acc[i][m] = 0.0f;
-                        if constexpr (XREG) {
-                            segment_sums<F, NI, MC>(cur.w[t], kc,
-                                                    [&](int a, int m, int vv) { return xr[a][m][vv]; }, acc);
+                            for (int i = 0; i < NI; ++i) acc[0][0][i] = a1[i][0];
                         } else {
-                            segment_sums<F, NI, MC>(
-                                cur.w[t], kc,
-                                [&](int a, int m, int vv) {
-                                    return *reinterpret_cast<const u4_t *>(xs + (size_t)m * K + xoff[a] + 8 * vv);
-                                },
-                                acc);
-                        }
+                            // rows x columns are the independent chains;
+                            // segments go one after another so only one
+                            // segment's codes and activations are live
 #pragma unroll
-                        for (int m = 0; m < MC; ++m) {
-                            float v[NIP];
+                            for (int i = 0; i < NI; ++i) {
+                                u4_t wr[R];
 #pragma unroll
-                            for (int a = 0; a < NIP; ++a) {
-                                float val = 0.0f;
-                                if (a < NI) {
-                                    if constexpr (F == FMT_INT2) val = acc[a][m];
-                                    else if constexpr (F == FMT_INT4) val = seg_scale<F>(cur.seg[t][a]) * acc[a][m];
-                                    else val = acc[a][m] * seg_scale<F>(cur.seg[t][a]);
-                                    // segments past the row end are the tree's +0 padding
-                                    val = (q + RL * a < nseg) ? val : 0.0f;
-                                }
-                                v[a] = val;
+                                for (int r = 0; r < R; ++r) wr[r] = cur.w[t][r][i];
+                                float ar[R][MC];
+#pragma unroll
+                                for (int r = 0; r < R; ++r)
+#pragma unroll
+                                    for (int m = 0; m < MC; ++m) ar[r][m] = 0.0f;
+                                segment_sums_rows<F, R, MC>(wr, kc, xs, xoff[i], K, ar);
+#pragma unroll
+                                for (int r = 0; r < R; ++r)
+#pragma unroll
+                                    for (int m = 0; m < MC; ++m) acc[r][m][i] = ar[r][m];
+                                // keep the next segment's LDS reads from being
+                                // scheduled ahead of this one (register budget)
+                                __builtin_amdgcn_sched_barrier(0);
                             }
-                            tot[t][m] = fo_tree<RL, NIP>(v, P2);
                         }
-                    }
-                    float rs[NMAT];
 #pragma unroll
-                    for (int t = 0; t < NMAT; ++t) rs[t] = half_bits_to_f32((uint16_t)cur.rs[t]);
-                    epi(rg * RPG + rsub, q, tot, rs);
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int m = 0; m < MC; ++m) tot[r][t][m] = finish(acc[r][m], cur.seg[t][r]);
+                    }
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        float rs[NMAT];
+#pragma unroll
+                        for (int t = 0; t < NMAT; ++t) rs[t] = half_bits_to_f32((uint16_t)cur.rs[t][r]);
+                        epi((u * R + r) * RPG + rsub, q, tot[r], rs);
+                    }
                 }
+                if constexpr (!kRefillFirst) load(slot[d]);
             }
         }
     }
@@ -331,7 +395,7 @@ __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict_
     const int m0 = blockIdx.y * MC;
     const uint8_t *const w1[1] = {wq};
     const void *const s1[1] = {sc};
-    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>()> eng(w1, s1, N, K);
+    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG>()> eng(w1, s1, N, K);
     XStage<MC> xst;
     xst.load(x, M, K, m0);
     eng.prefetch();
@@ -445,7 +509,7 @@ __global__ __launch_bounds__(kBlock) void k_fo_gateup(
     const uint8_t *const w2[2] = {reinterpret_cast<const uint8_t *>(wq_gate),
                                   reinterpret_cast<const uint8_t *>(wq_up)};
     const void *const s2[2] = {s_gate, s_up};
-    FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 2, ring_depth<NI, 2>()> eng(w2, s2, N, K);
+    FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 2, ring_depth<NI, 2>(), rows_block<MC, XREG>()> eng(w2, s2, N, K);
     eng.prefetch();
     rmsnorm_prologue<MC>(x, residual, gamma, residual_out, eps, M, K, m0, xs, xs, inv_s);
     GateUpEpi<MC> epi{out, M, N, m0};
@@ -503,7 +567,7 @@ __global__ __launch_bounds__(kBlock) void k_fo_argmax(const uint32_t *__restrict
     const int m0 = blockIdx.y * MC;
     const uint8_t *const w1[1] = {reinterpret_cast<const uint8_t *>(wq)};
     const void *const s1[1] = {scale};
-    FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>()> eng(w1, s1, N, K);
+    FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG>()> eng(w1, s1, N, K);
     XStage<MC> xst;
     xst.load(x, M, K, m0);
     eng.prefetch();
@@ -583,7 +647,27 @@ static int grid_for(Kern kernel, size_t lds, int N, int RL, int depth) {
 
 // M = 1 keeps the activation slice in registers (MC = 1); wider M uses
 // chunks of 4 activation rows read from LDS.
-constexpr int kMcWide = 4;
+// Activation rows per workgroup for M > 1: 4, or 2 when a lane holds three or
+// more segments (fewer live values per segment keep the kernel out of
+// scratch).
+#ifndef QMV_MCW
+#define QMV_MCW 4
+#endif
+#ifndef QMV_MCW3
+#define QMV_MCW3 2
+#endif
+template <int NI>
+constexpr int mc_wide() {
+    return NI >= 3 ? QMV_MCW3 : QMV_MCW;
+}
+
+// Units (row blocks) per wave aimed at when sizing a launch that reads the
+// activations from LDS: every workgroup stages its activation chunk once,
+// so fewer, longer-lived workgroups amortise that copy.
+#ifndef QMV_WIDE_UNITS
+#define QMV_WIDE_UNITS 2
+#endif
+constexpr int kWideUnits = QMV_WIDE_UNITS;
 
 // Registers a lane spends on its activation slice when MC = 1 (16-byte
 // vectors x 4 VGPRs); above this budget the slice is read from LDS instead.
@@ -592,8 +676,8 @@ constexpr int kXregBudget = QMV_XREG_BUDGET;
 // Dynamic LDS per workgroup is kept within 64 KB; chunks of kMcWide
 // activation rows are used when they fit, single rows otherwise.
 constexpr size_t kLdsBudget = 65536;
-static inline bool wide_fits(int K, int copies) {
-    return (size_t)copies * kMcWide * K * 2 + 64 * kMcWide <= kLdsBudget;
+static inline bool wide_fits(int K, int copies, int mc) {
+    return (size_t)copies * mc * K * 2 + 64 * mc <= kLdsBudget;
 }
 
 template <int F, int NI>
@@ -611,16 +695,17 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
         const size_t lds = (size_t)a.K * 2;
         hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), 1), dim3(kBlock), lds, st, wq, a.sc,
                            a.x, a.y, a.y_dtype, a.M, a.N, a.K);
-    } else if (wide_fits(a.K, 1)) {
-        auto k = k_fo_matvec<F, RL, NI, NIP, kMcWide, false>;
-        const size_t lds = (size_t)kMcWide * a.K * 2;
-        const int gy = (a.M + kMcWide - 1) / kMcWide;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), gy), dim3(kBlock), lds, st, wq, a.sc,
+    } else if (wide_fits(a.K, 1, mc_wide<NI>())) {
+        constexpr int MCW = mc_wide<NI>();
+        auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false>;
+        const size_t lds = (size_t)MCW * a.K * 2;
+        const int gy = (a.M + MCW - 1) / MCW;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), gy), dim3(kBlock), lds, st, wq, a.sc,
                            a.x, a.y, a.y_dtype, a.M, a.N, a.K);
     } else {
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
         const size_t lds = (size_t)a.K * 2;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), a.M), dim3(kBlock), lds, st, wq, a.sc,
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), a.M), dim3(kBlock), lds, st, wq, a.sc,
                            a.x, a.y, a.y_dtype, a.M, a.N, a.K);
     }
     return hipGetLastError();
@@ -659,7 +744,8 @@ hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t st) {
 template <int RL, int NI, int NIP>
 static hipError_t gu_shape(const GateUpArgs &a, hipStream_t st) {
     constexpr int D = ring_depth<NI, 2>();
-    if (a.M == 1 || !wide_fits(a.K, 1)) {
+    constexpr int MCW = mc_wide<NI>();
+    if (a.M == 1 || !wide_fits(a.K, 1, MCW)) {
         const size_t lds = (size_t)a.K * 2 + 64;
         if (a.M == 1) {
             auto k = k_fo_gateup<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>;
@@ -668,15 +754,15 @@ static hipError_t gu_shape(const GateUpArgs &a, hipStream_t st) {
                                a.s_up, a.out, a.M, a.N, a.K);
         } else {
             auto k = k_fo_gateup<RL, NI, NIP, 1, false>;
-            hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), a.M), dim3(kBlock), lds, st, a.x,
+            hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), a.M), dim3(kBlock), lds, st, a.x,
                                a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
                                a.s_up, a.out, a.M, a.N, a.K);
         }
     } else {
-        auto k = k_fo_gateup<RL, NI, NIP, kMcWide, false>;
-        const size_t lds = (size_t)kMcWide * a.K * 2 + 64 * kMcWide;
-        const int gy = (a.M + kMcWide - 1) / kMcWide;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), gy), dim3(kBlock), lds, st, a.x,
+        auto k = k_fo_gateup<RL, NI, NIP, MCW, false>;
+        const size_t lds = (size_t)MCW * a.K * 2 + 64 * MCW;
+        const int gy = (a.M + MCW - 1) / MCW;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), gy), dim3(kBlock), lds, st, a.x,
                            a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
                            a.s_up, a.out, a.M, a.N, a.K);
     }
@@ -690,8 +776,8 @@ hipError_t launch_fo_gateup(const GateUpArgs &a, hipStream_t st) {
 }
 
 // Activation rows per argmax workgroup chunk, and the number of chunks.
-static void argmax_chunks(int M, int K, int &mc, int &gy) {
-    mc = (M > 1 && wide_fits(K, 1)) ? kMcWide : 1;
+static void argmax_chunks(int M, int K, int mcw, int &mc, int &gy) {
+    mc = (M > 1 && wide_fits(K, 1, mcw)) ? mcw : 1;
     gy = (M + mc - 1) / mc;
 }
 
@@ -708,8 +794,9 @@ static hipError_t am_shape(const ArgmaxArgs &a, hipStream_t st) {
     constexpr int D = ring_depth<NI, 1>();
     uint32_t *counter = reinterpret_cast<uint32_t *>(a.ws);
     uint64_t *keys = reinterpret_cast<uint64_t *>(reinterpret_cast<uint8_t *>(a.ws) + kCounterBytes);
+    constexpr int MCW = mc_wide<NI>();
     int mc, gy;
-    argmax_chunks(a.M, a.K, mc, gy);
+    argmax_chunks(a.M, a.K, MCW, mc, gy);
     if (a.M == 1) {
         auto k = k_fo_argmax<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>;
         const size_t lds = (size_t)a.K * 2;
@@ -718,12 +805,12 @@ static hipError_t am_shape(const ArgmaxArgs &a, hipStream_t st) {
     } else if (mc == 1) {
         auto k = k_fo_argmax<RL, NI, NIP, 1, false>;
         const size_t lds = (size_t)a.K * 2;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), gy), dim3(kBlock), lds, st, a.wq,
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), gy), dim3(kBlock), lds, st, a.wq,
                            a.scale, a.x, a.idx, a.maxval, a.logits, a.M, a.N, a.K, keys, counter);
     } else {
-        auto k = k_fo_argmax<RL, NI, NIP, kMcWide, false>;
-        const size_t lds = (size_t)kMcWide * a.K * 2;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), gy), dim3(kBlock), lds, st, a.wq,
+        auto k = k_fo_argmax<RL, NI, NIP, MCW, false>;
+        const size_t lds = (size_t)MCW * a.K * 2;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), gy), dim3(kBlock), lds, st, a.wq,
                            a.scale, a.x, a.idx, a.maxval, a.logits, a.M, a.N, a.K, keys, counter);
     }
     return hipGetLastError();
