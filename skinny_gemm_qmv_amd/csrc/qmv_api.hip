@@ -126,7 +126,11 @@ qmv_status qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_t *x, 
     (void)workspace; (void)ws_bytes;
     qmv_status s = check_matvec(wq, e8m0, x, y, y_dtype, M, N, K, 32, mode);
     if (s != QMV_OK) return s;
-    if (mode == QMV_MODE_MFMA) return QMV_ERR_UNSUPPORTED;
+    if (mode == QMV_MODE_MFMA) {
+        if (M < 32) return QMV_ERR_UNSUPPORTED;
+        qmv::MatvecArgs a{2, wq, e8m0, x, y, (int)y_dtype, M, N, K};
+        return hip_status(qmv::launch_mxfp4_mfma(a, static_cast<hipStream_t>(stream)));
+    }
     return run_matvec(2, wq, e8m0, x, y, y_dtype, M, N, K, mode, stream);
 }
 

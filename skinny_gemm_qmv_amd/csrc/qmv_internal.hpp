@@ -30,6 +30,9 @@ struct MatvecArgs {
 
 hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t stream);
 
+// Matrix-core MXFP4 GEMM (tolerance class), 32 <= M <= 256.
+hipError_t launch_mxfp4_mfma(const MatvecArgs &a, hipStream_t stream);
+
 struct GateUpArgs {
     const uint16_t *x, *residual, *gamma;
     uint16_t *residual_out;
