@@ -110,8 +110,11 @@ __device__ __forceinline__ void int4_decode_word(uint32_t w, const DecodeConsts 
 
 // E8M0 block scale as an fp32 value: 2^(E-127), exact for E in 0..254
 // (E = 0 is the subnormal 2^-127), NaN for E = 255.
+// Branch-free: the exponent field is E, and the mantissa bit 22 is set for
+// E = 0 (giving 2^-127) and E = 255 (turning +inf into a quiet NaN).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-    return e == 0u ? u2f(0x00400000u) : (e == 255u ? u2f(0x7FC00000u) : u2f(e << 23));
+    const uint32_t special = (e == 0u || e == 255u) ? 0x00400000u : 0u;
+    return u2f((e << 23) | special);
 }
 
 // Inner step for the NS segments a lane holds in one row group, for MC

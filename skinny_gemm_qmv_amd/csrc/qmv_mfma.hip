@@ -13,24 +13,26 @@
 // in fp32.  The order of that sum is the matrix core's, not the fixed order:
 // this mode belongs to the tolerance class (relative L2 error <= 2e-3).
 //
-// Work split (MI355X: 256 CUs in 8 XCDs, one matrix core per SIMD):
-//  * The output is cut into blocks of BM = 64 activation rows (4 m-tiles of
-//    16) by a contiguous range of 16-row weight tiles.  With S = ceil(M/64)
-//    row blocks, 256/S ranges make one workgroup per CU.  Workgroups of the
-//    same weight range get block indices that are equal modulo 8, i.e. the
-//    same XCD (workgroups go to XCDs round-robin), so the S reads of a weight
-//    range meet in that XCD's L2 instead of going to HBM S times.
-//  * Per chunk of K (128 = four MXFP4 blocks) the workgroup copies its
-//    activation tile [64][128] bf16 to LDS with fully coalesced loads
-//    (double buffered, one barrier per chunk).
-//  * The 4 waves split the weight tiles of the range (tile t goes to wave
-//    t mod 4), so every weight byte is loaded and dequantized once; each
-//    wave multiplies its tiles by all 4 m-tiles read from LDS.
-//  * Lane group g = lane / 16 holds the whole 16-byte MXFP4 block 4c + g of
-//    its weight row (one dwordx4 plus the scale byte); sub-step j hands dword
-//    j (8 codes) to the MFMA, and the A fragment of lane group g, sub-step j
-//    is read from the same k range, so both operands map (g, element e) of
-//    sub-step j to k = 128c + 32g + 8j + e.
+// Work split (MI355X: 256 CUs, one matrix core per SIMD):
+//  * Workgroup b owns a contiguous range of 16-row weight tiles (at most one
+//    workgroup per CU, so each weight byte is read from HBM once) and all M
+//    activation rows; its WV waves split M (MW m-tiles of 16 rows each).
+//  * K advances in chunks of 128 = four MXFP4 blocks.  Every load is laid
+//    out for the memory system: a weight tile's chunk (16 rows x 64 bytes)
+//    is read by four consecutive lanes per row, an activation row's chunk
+//    (256 bytes) by sixteen consecutive lanes.
+//  * The weight tiles of a chunk are loaded once per workgroup (tile i by
+//    wave i mod WV) into a shared LDS buffer (double buffered, one barrier
+//    per chunk); each wave keeps its own activation rows in a private LDS
+//    pad.  Both are read back in the MFMA layout.
+//  * Lane group g = lane / 16 reads the whole 16-byte MXFP4 block 4c + g of
+//    weight row l % 16 and its scale; sub-step j dequantizes dword j (8 codes)
+//    and the A fragment of lane group g, sub-step j comes from the same k
+//    range, so both operands map (g, element e) of sub-step j to
+//    k = 128c + 32g + 8j + e.
+//  * Each wave dequantizes every tile of the range (4/MW conversions per
+//    MFMA); two waves per SIMD (WV = 8) let one wave's conversions overlap
+//    the other's matrix work.
 #include "qmv_device.hpp"
 #include "qmv_internal.hpp"
 
@@ -40,199 +42,227 @@ typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaWaves = 4;
 constexpr uint32_t kOob = 0xFFFFFFF0u;  // past every buffer: loads return 0
 #ifndef QMV_MFMA_WAUX
-#define QMV_MFMA_WAUX 2
+#define QMV_MFMA_WAUX 0
 #endif
 
-constexpr int kMT = 4;                  // m-tiles (of 16 rows) per workgroup
-constexpr int kXRow = 128 * 2 + 16;     // LDS bytes per activation row of a chunk (+16: bank spread)
-constexpr int kXBuf = kMT * 16 * kXRow;  // one LDS buffer
+constexpr int kXRow = 128 * 2 + 16;  // LDS bytes per activation row of a chunk (+16: bank spread)
+constexpr int kWRow = 64 + 16;       // LDS bytes per weight row of a chunk (+16: conflict-free reads)
+constexpr int kWTile = 16 * kWRow;   // one 16-row weight tile of a chunk
 
-// Loads of one chunk: the weight tiles of a wave (dwordx4 + scale byte per
-// lane and tile) and this thread's 64-byte share of the activation tile.
-template <int NW>
+// Loads of one chunk held by a wave: its weight tile slots (dwordx4 + scale
+// byte per lane) and its activation rows (MW m-tiles x 4 dwordx4 per lane).
+template <int WT, int MW>
 struct ChunkSlot {
-    u4_t w[NW];
-    uint32_t e[NW];
-    u4_t x[4];
+    u4_t w[WT];
+    uint32_t e[WT];
+    u4_t x[MW][4];
 };
 
-// Chunks in flight besides the one being multiplied.  Both the weights (from
-// HBM) and the activation tile (from L2) travel D chunks ahead; a wave with
-// few tiles has little matrix work per chunk to cover that latency with.
-template <int NW>
+// Chunks in flight besides the one being multiplied.
+template <int WV, int MW>
 constexpr int mfma_depth() {
-    return NW <= 2 ? 4 : (NW <= 4 ? 3 : 2);
+    return WV == 4 ? 4 : (MW == 1 ? 3 : 2);
 }
 
-template <int NW>
-__global__ __launch_bounds__(kMfmaWaves * 64) void k_mxfp4_mfma(
+template <int WV, int MW, int NB>
+__global__ __launch_bounds__(WV * 64) void k_mxfp4_mfma(
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ e8m0, const uint16_t *__restrict__ x,
-    void *y, int y_dtype, int M, int N, int K, int NT, int S, int ranges, int xcd_map) {
-    constexpr int D = mfma_depth<NW>();
-    __shared__ __align__(16) uint8_t xs[2][kXBuf];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    void *y, int y_dtype, int M, int N, int K, int NT, int ranges) {
+    constexpr int D = mfma_depth<WV, MW>();
+    constexpr int WT = (NB + WV - 1) / WV;  // tile slots loaded by each wave
+    __shared__ __align__(16) uint8_t wbuf[2][NB][kWTile];
+    __shared__ __align__(16) uint8_t sbuf[2][NB][64];
+    __shared__ __align__(16) uint8_t xpad[WV][MW * 16 * kXRow];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    // block index -> (weight range, row block); see the work split above
-    const int b = blockIdx.x;
-    int rg, sb;
-    if (xcd_map) {
-        sb = (b >> 3) % S;
-        rg = (b & 7) + 8 * (b / (8 * S));
-    } else {
-        sb = b % S;
-        rg = b / S;
-    }
-    const int t0 = (int)(((long)rg * NT) / ranges);
-    const int t1 = (int)(((long)(rg + 1) * NT) / ranges);
-    const int m0 = sb * kMT * 16;
+    const int lrow = lane >> 2, lpc = lane & 3;  // weight load layout
+    const int t0 = (int)(((long)blockIdx.x * NT) / ranges);
+    const int t1 = (int)(((long)(blockIdx.x + 1) * NT) / ranges);  // t1 - t0 <= NB (host)
+    const int m0w = wave * MW * 16;  // first activation row of this wave
 
     const int nseg = K >> 5;
     const int nchunk = (nseg + 3) >> 2;
     const uint32_t row_bytes = (uint32_t)K >> 1;
+    const uint32_t xrow_bytes = (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(wq), 0, (uint32_t)N * row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t re =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(e8m0), 0, (uint32_t)N * nseg, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(x), 0, (uint32_t)M * (uint32_t)K * 2u, 0x00020000);
+        const_cast<uint16_t *>(x), 0, (uint32_t)M * xrow_bytes, 0x00020000);
 
-    // this wave's tiles: t0 + wave + 4i, i < NW
-    uint32_t wrow[NW], erow[NW];
-    bool tok[NW];
+    // weight tile slots of this wave: slot i = wave + WV*s of the range
+    uint32_t wrow[WT], erow[WT];
+    bool sok[WT], tok[WT];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int t = t0 + wave + 4 * i;
-        const uint32_t n = (uint32_t)t * 16u + r16;
-        tok[i] = t < t1;
-        wrow[i] = n * row_bytes + 16u * g;
-        erow[i] = n * (uint32_t)nseg + g;
+    for (int s = 0; s < WT; ++s) {
+        const int i = wave + WV * s;
+        const uint32_t n = (uint32_t)(t0 + i) * 16u + lrow;
+        sok[s] = i < NB;             // slot exists (uniform)
+        tok[s] = sok[s] && t0 + i < t1;  // and holds a tile of this range
+        wrow[s] = n * row_bytes + 16u * lpc;
+        erow[s] = n * (uint32_t)nseg + lpc;
     }
-    // activation tile copy: thread -> (row tid/4, 64-byte quarter tid%4) of the
-    // [64][256 B] chunk; rows >= M read 0 (past the buffer)
-    const int xr_row = tid >> 2, xr_q = tid & 3;
-    const uint32_t xg = (uint32_t)(m0 + xr_row) * (uint32_t)K * 2u + 64u * xr_q;
-    auto load = [&](ChunkSlot<NW> &sl, int c) {
-        const bool segok = 4 * c + g < nseg;  // the last chunk may hold fewer than 4 blocks
+    // activation rows of this wave: load q of m-tile mw covers rows
+    // mw*16 + 4q + lane/16; rows >= M read 0 (past the buffer)
+    const uint32_t xbase = (uint32_t)(m0w + (lane >> 4)) * xrow_bytes + 16u * (lane & 15);
+
+    auto load = [&](ChunkSlot<WT, MW> &sl, int c) {
+        const bool segok = 4 * c + lpc < nseg;  // the last chunk may hold fewer than 4 blocks
 #pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const bool ok = segok && tok[i];
-            sl.w[i] = __builtin_bit_cast(
-                u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wrow[i] + 64u * c : kOob, 0, QMV_MFMA_WAUX));
-            sl.e[i] = __builtin_amdgcn_raw_buffer_load_b8(re, ok ? erow[i] + 4u * c : kOob, 0, 0);
+        for (int s = 0; s < WT; ++s) {
+            const bool ok = segok && tok[s];
+            sl.w[s] = __builtin_bit_cast(
+                u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wrow[s] + 64u * c : kOob, 0, QMV_MFMA_WAUX));
+            sl.e[s] = __builtin_amdgcn_raw_buffer_load_b8(re, ok ? erow[s] + 4u * c : kOob, 0, 0);
         }
-        // chunks past the end read nothing (out of range)
-        const uint32_t xo = c < nchunk ? xg + 256u * c : kOob;
+        const bool cok = c < nchunk;  // chunks past the end read nothing
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sl.x[j] = __builtin_bit_cast(
-                u4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xo == kOob ? kOob : xo + 16u * j, 0, 0));
+        for (int mw = 0; mw < MW; ++mw)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sl.x[mw][q] = __builtin_bit_cast(
+                    u4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                              rx, cok ? xbase + (uint32_t)(mw * 16 + 4 * q) * xrow_bytes + 256u * c : kOob, 0, 0));
     };
 
-    f4_t acc[kMT][NW];
+    f4_t acc[MW][NB];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mw = 0; mw < MW; ++mw)
 #pragma unroll
-        for (int i = 0; i < NW; ++i) acc[mt][i] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < NB; ++i) acc[mw][i] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    ChunkSlot<NW> slot[D];
+    ChunkSlot<WT, MW> slot[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) load(slot[d], d);
 
-    // Chunk c: its activations go to LDS buffer c&1, one barrier makes them
-    // visible (every wave has then also finished chunk c-1, the last reader of
-    // the other buffer, and chunk c-2, the last reader of this one), the slot
-    // is refilled with chunk c+D, and the tile products are accumulated.
-    for (int c0 = 0; c0 < nchunk; c0 += D) {
+    uint8_t *xp = xpad[wave];
+    const bool active = m0w < M;  // uniform: this wave has activation rows
+    // Chunk c: the wave's weight slots go to buffer c&1 and its activation
+    // rows to its pad, one barrier publishes the weights (every wave has
+    // then also finished chunk c-1, which read the other buffer, and chunk
+    // c-2, the last reader of this one; the pad is private and LDS accesses
+    // of a wave complete in order), the slot is refilled with chunk c+D, and
+    // the tile products are accumulated.
+    auto step = [&](ChunkSlot<WT, MW> &sl, int c) {
+        const ChunkSlot<WT, MW> cur = sl;
+        uint8_t(*wb)[kWTile] = wbuf[c & 1];
+        uint8_t(*sb)[64] = sbuf[c & 1];
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int c = c0 + d;
-            if (c < nchunk) {  // uniform across the workgroup
-                const ChunkSlot<NW> cur = slot[d];
-                uint8_t *xb = xs[c & 1];
+        for (int s = 0; s < WT; ++s)
+            if (sok[s]) {
+                *reinterpret_cast<u4_t *>(&wb[wave + WV * s][lrow * kWRow + 16 * lpc]) = cur.w[s];
+                sb[wave + WV * s][lrow * 4 + lpc] = (uint8_t)cur.e[s];
+            }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<u4_t *>(&xb[xr_row * kXRow + 64 * xr_q + 16 * j]) = cur.x[j];
-                __syncthreads();
-                load(slot[d], c + D);
-                float sc[NW];
+        for (int mw = 0; mw < MW; ++mw)
 #pragma unroll
-                for (int i = 0; i < NW; ++i) sc[i] = e8m0_to_f32(cur.e[i]);
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<u4_t *>(&xp[(mw * 16 + 4 * q + (lane >> 4)) * kXRow + 16 * (lane & 15)]) =
+                    cur.x[mw][q];
+        __syncthreads();
+        load(sl, c + D);  // past the end: out-of-range offsets, no traffic
+        if (active) {
+            u4_t braw[NB];
+            float sc[NB];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf8_t bw[NW];
+            for (int i = 0; i < NB; ++i) {
+                braw[i] = *reinterpret_cast<const u4_t *>(&wb[i][r16 * kWRow + 16 * g]);
+                sc[i] = e8m0_to_f32(sb[i][r16 * 4 + g]);
+            }
 #pragma unroll
-                    for (int i = 0; i < NW; ++i) {
-                        const uint32_t wd = cur.w[i][j];
-                        const bf2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 0);
-                        const bf2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 1);
-                        const bf2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 2);
-                        const bf2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 3);
-                        bw[i] = bf8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-                    }
+            for (int j = 0; j < 4; ++j) {
+                bf8_t a[MW];
 #pragma unroll
-                    for (int mt = 0; mt < kMT; ++mt) {
-                        const bf8_t a = __builtin_bit_cast(
-                            bf8_t, *reinterpret_cast<const u4_t *>(xb + (mt * 16 + r16) * kXRow + 64 * g + 16 * j));
+                for (int mw = 0; mw < MW; ++mw)
+                    a[mw] = __builtin_bit_cast(
+                        bf8_t, *reinterpret_cast<const u4_t *>(&xp[(mw * 16 + r16) * kXRow + 64 * g + 16 * j]));
 #pragma unroll
-                        for (int i = 0; i < NW; ++i)
-                            acc[mt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[i], acc[mt][i], 0, 0, 0);
-                    }
+                for (int i = 0; i < NB; ++i) {
+                    const uint32_t wd = braw[i][j];
+                    const bf2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 0);
+                    const bf2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 1);
+                    const bf2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 2);
+                    const bf2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 3);
+                    const bf8_t bw = bf8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+#pragma unroll
+                    for (int mw = 0; mw < MW; ++mw)
+                        acc[mw][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mw], bw, acc[mw][i], 0, 0, 0);
                 }
             }
         }
+    };
+    // Whole groups of D chunks without conditions (loads issued on every
+    // path keep the compiler's count of outstanding loads exact, so each
+    // chunk waits only for its own data), then the remaining < D chunks.
+    int c = 0;
+    for (; c + D <= nchunk; c += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) step(slot[d], c + d);
     }
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        if (c + d < nchunk) step(slot[d], c + d);
 
     // D[i][j] of a 16x16 tile: lane l holds rows 4(l/16) .. 4(l/16)+3 of column l%16.
+    if (!active) return;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const int n = (t0 + wave + 4 * i) * 16 + r16;
-        if (!tok[i] || n >= N) continue;
+    for (int i = 0; i < NB; ++i) {
+        const int n = (t0 + i) * 16 + r16;
+        if (t0 + i >= t1 || n >= N) continue;
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
+        for (int mw = 0; mw < MW; ++mw)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int m = m0 + mt * 16 + 4 * g + v;
-                if (m < M) store_out(y, (size_t)m * N + n, acc[mt][i][v], y_dtype);
+                const int m = m0w + mw * 16 + 4 * g + v;
+                if (m < M) store_out(y, (size_t)m * N + n, acc[mw][i][v], y_dtype);
             }
     }
 }
 
-// Tiles per wave compiled (a range holds up to 4 * NW tiles).
-constexpr int kMfmaMaxNw = 6;
+// Tiles per workgroup compiled; the host picks the smallest that covers
+// ceil(NT / grid).
+constexpr int kMfmaMaxNb = 8;
 
-template <int NW>
-static hipError_t mfma_launch(const MatvecArgs &a, int NT, int S, int ranges, hipStream_t st) {
-    const int xcd_map = (ranges % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((k_mxfp4_mfma<NW>), dim3(S * ranges), dim3(kMfmaWaves * 64), 0, st,
+template <int WV, int MW, int NB>
+static hipError_t mfma_launch(const MatvecArgs &a, int NT, int ranges, hipStream_t st) {
+    hipLaunchKernelGGL((k_mxfp4_mfma<WV, MW, NB>), dim3(ranges), dim3(WV * 64), 0, st,
                        reinterpret_cast<const uint8_t *>(a.wq), reinterpret_cast<const uint8_t *>(a.sc), a.x,
-                       a.y, a.y_dtype, a.M, a.N, a.K, NT, S, ranges, xcd_map);
+                       a.y, a.y_dtype, a.M, a.N, a.K, NT, ranges);
     return hipGetLastError();
+}
+
+template <int WV, int MW>
+static hipError_t mfma_nb(const MatvecArgs &a, int NT, int ranges, int nb, hipStream_t st) {
+    if (nb <= 1) return mfma_launch<WV, MW, 1>(a, NT, ranges, st);
+    if (nb <= 2) return mfma_launch<WV, MW, 2>(a, NT, ranges, st);
+    if (nb <= 3) return mfma_launch<WV, MW, 3>(a, NT, ranges, st);
+    if (nb <= 4) return mfma_launch<WV, MW, 4>(a, NT, ranges, st);
+    if (MW > 1 || nb <= 6) return mfma_launch<WV, MW, 6>(a, NT, ranges, st);
+    return mfma_launch<WV, MW, (MW > 1 ? 6 : 8)>(a, NT, ranges, st);
 }
 
 hipError_t launch_mxfp4_mfma(const MatvecArgs &a, hipStream_t st) {
     if (a.fmt != FMT_MXFP4 || a.M < 32 || a.M > 256 || a.K % 32 != 0) return hipErrorInvalidValue;
     const int NT = (a.N + 15) / 16;
-    const int S = (a.M + kMT * 16 - 1) / (kMT * 16);  // row blocks of 64
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    int ranges = cus / S;
-    if (ranges < 1) ranges = 1;
-    if (ranges > NT) ranges = NT;
-    int per = (NT + ranges - 1) / ranges;  // tiles per range (at most)
-    if (per > 4 * kMfmaMaxNw) {
-        per = 4 * kMfmaMaxNw;
-        ranges = (NT + per - 1) / per;
+    const int mt = (a.M + 15) / 16;
+    // two m-tiles per wave leave registers for 6 tiles per workgroup
+    const int max_nb = mt > 8 ? 6 : kMfmaMaxNb;
+    int ranges = NT < cus ? NT : cus;
+    int nb = (NT + ranges - 1) / ranges;
+    if (nb > max_nb) {
+        nb = max_nb;
+        ranges = (NT + nb - 1) / nb;
     }
-    const int nw = (per + 3) / 4;  // tiles per wave (at most)
-    if (nw <= 1) return mfma_launch<1>(a, NT, S, ranges, st);
-    if (nw <= 2) return mfma_launch<2>(a, NT, S, ranges, st);
-    if (nw <= 3) return mfma_launch<3>(a, NT, S, ranges, st);
-    if (nw <= 4) return mfma_launch<4>(a, NT, S, ranges, st);
-    return mfma_launch<6>(a, NT, S, ranges, st);
+    // every range t0..t1 then spans at most nb tiles
+    if (mt <= 4) return mfma_nb<4, 1>(a, NT, ranges, nb, st);
+    if (mt <= 8) return mfma_nb<8, 1>(a, NT, ranges, nb, st);
+    return mfma_nb<8, 2>(a, NT, ranges, nb, st);
 }
 
 }  // namespace qmv
