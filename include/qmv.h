@@ -57,8 +57,15 @@
  *      the fp32 row scale.  Every fp32 operation is one IEEE
  *      round-to-nearest-even operation; denormals are kept.
  *  QMV_MODE_SPLITK opt-in tolerant mode: relative L2 error <= 2e-3 against
- *      the fixed order over the whole output; the K range may be split over
- *      workgroups and the summation order differs.
+ *      the fixed order over the whole output.  The library splits K into S
+ *      ranges of whole segments (S <= 16, chosen from the shape so that short
+ *      N still fills the GPU; S = 1 when N alone does, and then the call runs
+ *      the fixed-order kernel and needs no workspace).  Each range's sum (in
+ *      the fixed order restricted to that range, before the int2 row scale)
+ *      goes to the workspace as fp32 [S][M][N]; a second kernel adds the S
+ *      partials in increasing range order and applies the int2 row scale, so
+ *      results are deterministic.  Workspace: qmv_workspace_size(op, M, N, K,
+ *      QMV_MODE_SPLITK) bytes, 256-byte aligned, no initialisation needed.
  *  QMV_MODE_MFMA   opt-in tolerant mode (relative L2 <= 2e-3) on the matrix
  *      cores; qmm_mxfp4 with M >= 32 only.
  *  A mode an entry point does not support returns QMV_ERR_UNSUPPORTED; there

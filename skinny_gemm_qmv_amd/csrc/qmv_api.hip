@@ -83,6 +83,11 @@ size_t qmv_workspace_size(qmv_op op, int M, int N, int K, qmv_mode mode) {
         if (mode != QMV_MODE_FIXED || !valid_shape(M, N, K, 64)) return 0;
         return qmv::argmax_workspace_bytes(M, N, K);
     }
+    if (mode == QMV_MODE_SPLITK && (op == QMV_OP_INT2 || op == QMV_OP_INT4 || op == QMV_OP_MXFP4)) {
+        const int kmul = op == QMV_OP_INT2 ? 64 : 32;
+        if (!valid_shape(M, N, K, kmul)) return 0;
+        return qmv::splitk_workspace_bytes((int)op, M, N, K);
+    }
     return 0;
 }
 
@@ -94,36 +99,42 @@ qmv_status qmv_workspace_init(void *ws, size_t bytes, void *stream) {
 }
 
 static qmv_status run_matvec(int fmt, const void *wq, const void *sc, const uint16_t *x, void *y,
-                             qmv_dtype dt, int M, int N, int K, qmv_mode mode, void *stream) {
-    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+                             qmv_dtype dt, int M, int N, int K, qmv_mode mode, void *ws, size_t ws_bytes,
+                             void *stream) {
     qmv::MatvecArgs a{fmt, wq, sc, x, y, (int)dt, M, N, K};
+    if (mode == QMV_MODE_SPLITK) {
+        const size_t need = qmv::splitk_workspace_bytes(fmt, M, N, K);
+        if (need > 0) {
+            if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
+            if (!aligned(ws, 256)) return QMV_ERR_ALIGNMENT;
+        }
+        return hip_status(qmv::launch_splitk_matvec(a, ws, static_cast<hipStream_t>(stream)));
+    }
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
     return hip_status(qmv::launch_fo_matvec(a, static_cast<hipStream_t>(stream)));
 }
 
 qmv_status qmv_int2(const uint32_t *wq, const uint16_t *scale, const uint16_t *x, void *y,
                     qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
                     size_t ws_bytes, void *stream) {
-    (void)workspace; (void)ws_bytes;
     qmv_status s = check_matvec(wq, scale, x, y, y_dtype, M, N, K, 64, mode);
     if (s != QMV_OK) return s;
     if (mode == QMV_MODE_MFMA) return QMV_ERR_UNSUPPORTED;
-    return run_matvec(0, wq, scale, x, y, y_dtype, M, N, K, mode, stream);
+    return run_matvec(0, wq, scale, x, y, y_dtype, M, N, K, mode, workspace, ws_bytes, stream);
 }
 
 qmv_status qmv_int4(const uint32_t *wq, const uint16_t *scales, const uint16_t *x, void *y,
                     qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
                     size_t ws_bytes, void *stream) {
-    (void)workspace; (void)ws_bytes;
     qmv_status s = check_matvec(wq, scales, x, y, y_dtype, M, N, K, 32, mode);
     if (s != QMV_OK) return s;
     if (mode == QMV_MODE_MFMA) return QMV_ERR_UNSUPPORTED;
-    return run_matvec(1, wq, scales, x, y, y_dtype, M, N, K, mode, stream);
+    return run_matvec(1, wq, scales, x, y, y_dtype, M, N, K, mode, workspace, ws_bytes, stream);
 }
 
 qmv_status qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_t *x, void *y,
                      qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
                      size_t ws_bytes, void *stream) {
-    (void)workspace; (void)ws_bytes;
     qmv_status s = check_matvec(wq, e8m0, x, y, y_dtype, M, N, K, 32, mode);
     if (s != QMV_OK) return s;
     if (mode == QMV_MODE_MFMA) {
@@ -131,7 +142,7 @@ qmv_status qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_t *x, 
         qmv::MatvecArgs a{2, wq, e8m0, x, y, (int)y_dtype, M, N, K};
         return hip_status(qmv::launch_mxfp4_mfma(a, static_cast<hipStream_t>(stream)));
     }
-    return run_matvec(2, wq, e8m0, x, y, y_dtype, M, N, K, mode, stream);
+    return run_matvec(2, wq, e8m0, x, y, y_dtype, M, N, K, mode, workspace, ws_bytes, stream);
 }
 
 qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *residual,

@@ -66,21 +66,23 @@ constexpr int kXpt = 4;
 template <int MC>
 struct XStage {
     u4_t v[kXpt];
-    __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int M, int K, int m0) {
-        const int per_row = K / 8;
+    // Row m of the staged chunk is x[m0 + m][0 .. len); `ld` is the row
+    // stride of x (len < ld when one K split is staged).
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int M, int ld, int len, int m0) {
+        const int per_row = len / 8;
 #pragma unroll
         for (int r = 0; r < kXpt; ++r) {
             const int e = threadIdx.x + r * blockDim.x;
             v[r] = u4_t{0u, 0u, 0u, 0u};
             if (e < MC * per_row) {
                 const int m = MC == 1 ? 0 : e / per_row, kk = e - m * per_row;
-                if (m0 + m < M) v[r] = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * K + 8 * kk);
+                if (m0 + m < M) v[r] = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * ld + 8 * kk);
             }
         }
     }
-    __device__ __forceinline__ void store(const uint16_t *__restrict__ x, uint16_t *xs, int M, int K,
+    __device__ __forceinline__ void store(const uint16_t *__restrict__ x, uint16_t *xs, int M, int ld, int len,
                                           int m0) {
-        const int per_row = K / 8;
+        const int per_row = len / 8;
 #pragma unroll
         for (int r = 0; r < kXpt; ++r) {
             const int e = threadIdx.x + r * blockDim.x;
@@ -89,8 +91,8 @@ struct XStage {
         for (int e = threadIdx.x + kXpt * blockDim.x; e < MC * per_row; e += blockDim.x) {
             const int m = MC == 1 ? 0 : e / per_row, kk = e - m * per_row;
             u4_t w = {0u, 0u, 0u, 0u};
-            if (m0 + m < M) w = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * K + 8 * kk);
-            *reinterpret_cast<u4_t *>(xs + (size_t)m * K + 8 * kk) = w;
+            if (m0 + m < M) w = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * ld + 8 * kk);
+            *reinterpret_cast<u4_t *>(xs + (size_t)m * len + 8 * kk) = w;
         }
     }
 };
@@ -163,22 +165,25 @@ struct FoEngine {
 
     static constexpr int kNT = 2;  // non-temporal: the weights are read once
 
+    // K_ is the number of codes this engine sums per row (a whole row, or one
+    // K split of nseg_row-segment rows starting at segment seg0).
     __device__ __forceinline__ FoEngine(const uint8_t *const (&wq)[NMAT], const void *const (&sc)[NMAT],
-                                        int N_, int K_)
+                                        int N_, int K_, int seg0 = 0, int nseg_row = 0)
         : N(N_), K(K_) {
         nseg = K / CODES;
+        if (nseg_row == 0) nseg_row = nseg;
         P2 = 1;
         while (P2 < nseg) P2 <<= 1;
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         q = lane % RL;
         rsub = lane / RL;
-        row_bytes = (uint32_t)nseg * 16u;
+        row_bytes = (uint32_t)nseg_row * 16u;
         const int total_rg = (N + RPG - 1) / RPG;
         total_units = (total_rg + R - 1) / R;
         stride = gridDim.x * kWaves;
         first = blockIdx.x * kWaves + wave;
         // bytes of scale data per row
-        srow = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u * nseg : (uint32_t)nseg);
+        srow = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u * nseg_row : (uint32_t)nseg_row);
         const uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);  // bytes per scale
 #pragma unroll
         for (int t = 0; t < NMAT; ++t) {
@@ -188,8 +193,8 @@ struct FoEngine {
                                                       (uint32_t)N * srow, 0x00020000);
         }
         const uint32_t n0 = (uint32_t)first * R * RPG + rsub;
-        woff = n0 * row_bytes + (uint32_t)q * 16u;
-        soff = n0 * srow + (F == FMT_INT2 ? 0u : (uint32_t)q * ssz);
+        woff = n0 * row_bytes + (uint32_t)(seg0 + q) * 16u;
+        soff = n0 * srow + (F == FMT_INT2 ? 0u : (uint32_t)(seg0 + q) * ssz);
         wstep = (uint32_t)stride * R * RPG * row_bytes;
         sstep = (uint32_t)stride * R * RPG * srow;
     }
@@ -367,9 +372,12 @@ struct FoEngine {
 
 // ---------------------------------------------------------------------------
 // Plain matvec / skinny GEMM.
+// Stores y (fixed order), or, in split-K mode, the split's partial sum
+// before the int2 row scale into part[m][n].
 template <int F, int MC>
 struct StoreEpi {
     void *y;
+    float *part;
     int y_dtype, M, N, m0;
     __device__ __forceinline__ void operator()(int n, int q, const float (&tot)[1][MC],
                                                const float (&rs)[1]) {
@@ -379,30 +387,58 @@ struct StoreEpi {
         for (int m = 0; m < MC; ++m) {
             if (m0 + m < M) {
                 float r = tot[0][m];
-                if constexpr (F == FMT_INT2) r = s * r;
-                store_out(y, (size_t)(m0 + m) * N + n, r, y_dtype);
+                if (part != nullptr) {
+                    part[(size_t)(m0 + m) * N + n] = r;
+                } else {
+                    if constexpr (F == FMT_INT2) r = s * r;
+                    store_out(y, (size_t)(m0 + m) * N + n, r, y_dtype);
+                }
             }
         }
     }
 };
 
+// blockIdx.z selects a K split of seg_split segments (one split covering the
+// whole row in fixed-order mode, part == nullptr); split z writes its partial
+// sums to part + z*M*N.
 template <int F, int RL, int NI, int NIP, int MC, bool XREG>
 __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict__ wq,
                                                       const void *__restrict__ sc,
                                                       const uint16_t *__restrict__ x, void *y,
-                                                      int y_dtype, int M, int N, int K) {
+                                                      int y_dtype, int M, int N, int K, int seg_split,
+                                                      float *part) {
     extern __shared__ __align__(16) uint16_t xs[];
+    constexpr int CODES = SegCodes<F>::v;
     const int m0 = blockIdx.y * MC;
+    const int nseg_row = K / CODES;
+    const int seg0 = blockIdx.z * seg_split;
+    const int nloc = nseg_row - seg0 < seg_split ? nseg_row - seg0 : seg_split;
+    const int klen = nloc * CODES;
+    const uint16_t *xz = x + (size_t)seg0 * CODES;
     const uint8_t *const w1[1] = {wq};
     const void *const s1[1] = {sc};
-    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG>()> eng(w1, s1, N, K);
+    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG>()> eng(w1, s1, N, klen, seg0,
+                                                                                       nseg_row);
     XStage<MC> xst;
-    xst.load(x, M, K, m0);
+    xst.load(xz, M, K, klen, m0);
     eng.prefetch();
-    xst.store(x, xs, M, K, m0);
+    xst.store(xz, xs, M, K, klen, m0);
     __syncthreads();
-    StoreEpi<F, MC> epi{y, y_dtype, M, N, m0};
+    StoreEpi<F, MC> epi{y, part == nullptr ? nullptr : part + (size_t)blockIdx.z * M * N, y_dtype, M, N, m0};
     eng.run(xs, epi);
+}
+
+// Split-K reduction: y[m][n] = (int2 row scale) * sum over z = 0 .. S-1 of
+// part[z][m][n], summed in increasing z.
+__global__ void k_splitk_reduce(const float *__restrict__ part, int S, int M, int N,
+                                const uint16_t *__restrict__ rscale, void *y, int y_dtype) {
+    const size_t total = (size_t)M * N;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+        float acc = part[e];
+        for (int z = 1; z < S; ++z) acc = acc + part[(size_t)z * total + e];
+        if (rscale != nullptr) acc = half_bits_to_f32(rscale[e % N]) * acc;
+        store_out(y, e, acc, y_dtype);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -569,9 +605,9 @@ __global__ __launch_bounds__(kBlock) void k_fo_argmax(const uint32_t *__restrict
     const void *const s1[1] = {scale};
     FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG>()> eng(w1, s1, N, K);
     XStage<MC> xst;
-    xst.load(x, M, K, m0);
+    xst.load(x, M, K, K, m0);
     eng.prefetch();
-    xst.store(x, xs, M, K, m0);
+    xst.store(x, xs, M, K, K, m0);
     __syncthreads();
     ArgmaxEpi<MC> epi{logits, M, N, m0, {}};
 #pragma unroll
@@ -629,7 +665,7 @@ __global__ void k_fill_zero(uint32_t *p, size_t words) {
 // device at once (occupancy x CUs), so every workgroup starts in the first
 // wave of the launch and none waits for a free CU.
 template <class Kern>
-static int grid_for(Kern kernel, size_t lds, int N, int RL, int depth) {
+static int grid_for(Kern kernel, size_t lds, long N, int RL, int depth) {
     const int rpg = 64 / RL;
     const long total_rg = ((long)N + rpg - 1) / rpg;
     long g = (total_rg + (long)kWaves * depth - 1) / ((long)kWaves * depth);
@@ -688,25 +724,34 @@ constexpr bool xreg_fits() {
 template <int F, int RL, int NI, int NIP>
 static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
     constexpr int D = ring_depth<NI, 1>();
+    constexpr int CODES = SegCodes<F>::v;
     const uint8_t *wq = reinterpret_cast<const uint8_t *>(a.wq);
+    const int seg_split = a.seg_split > 0 ? a.seg_split : a.K / CODES;
+    const int S = a.splits > 0 ? a.splits : 1;
+    const int klen = seg_split * CODES;  // activation values staged per column
+    // workgroups along x for one split: sized as if the S splits were S*N rows
+    auto gx = [&](auto k, size_t lds, int depth) {
+        const int g = grid_for(k, lds, (long)a.N * S, RL, depth);
+        return (g + S - 1) / S;
+    };
     if (a.M == 1) {
         constexpr bool xreg = xreg_fits<F, NI>();
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, xreg>;
-        const size_t lds = (size_t)a.K * 2;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), 1), dim3(kBlock), lds, st, wq, a.sc,
-                           a.x, a.y, a.y_dtype, a.M, a.N, a.K);
-    } else if (wide_fits(a.K, 1, mc_wide<NI>())) {
+        const size_t lds = (size_t)klen * 2;
+        hipLaunchKernelGGL(k, dim3(gx(k, lds, D), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
+                           a.N, a.K, seg_split, a.part);
+    } else if (wide_fits(klen, 1, mc_wide<NI>())) {
         constexpr int MCW = mc_wide<NI>();
         auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false>;
-        const size_t lds = (size_t)MCW * a.K * 2;
+        const size_t lds = (size_t)MCW * klen * 2;
         const int gy = (a.M + MCW - 1) / MCW;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), gy), dim3(kBlock), lds, st, wq, a.sc,
-                           a.x, a.y, a.y_dtype, a.M, a.N, a.K);
+        hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), gy, S), dim3(kBlock), lds, st, wq, a.sc, a.x,
+                           a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
     } else {
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
-        const size_t lds = (size_t)a.K * 2;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), a.M), dim3(kBlock), lds, st, wq, a.sc,
-                           a.x, a.y, a.y_dtype, a.M, a.N, a.K);
+        const size_t lds = (size_t)klen * 2;
+        hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), a.M, S), dim3(kBlock), lds, st, wq, a.sc, a.x,
+                           a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
     }
     return hipGetLastError();
 }
@@ -735,7 +780,7 @@ static hipError_t mv_mxfp4(const MatvecArgs &a, hipStream_t st) { return fo_matv
 hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t st) {
     const int codes = a.fmt == FMT_INT2 ? 64 : 32;
     LaneShape sh;
-    if (!pick_shape(a.K / codes, sh)) return hipErrorInvalidValue;
+    if (!pick_shape(a.seg_split > 0 ? a.seg_split : a.K / codes, sh)) return hipErrorInvalidValue;
     if (a.fmt == FMT_INT2) { QMV_SHAPE_SWITCH(mv_int2, a, st) }
     if (a.fmt == FMT_INT4) { QMV_SHAPE_SWITCH(mv_int4, a, st) }
     QMV_SHAPE_SWITCH(mv_mxfp4, a, st)
@@ -820,6 +865,56 @@ hipError_t launch_fo_argmax(const ArgmaxArgs &a, hipStream_t st) {
     LaneShape sh;
     if (!pick_shape(a.K / 64, sh)) return hipErrorInvalidValue;
     QMV_SHAPE_SWITCH(am_shape, a, st)
+}
+
+// Split-K plan: the smallest power-of-two split count (at most 16, at
+// least 4 segments per split) that gives every SIMD about four row groups;
+// K splits only pay when N alone leaves the GPU short of work.
+constexpr long kSplitTargetRowGroups = 4096;
+
+int splitk_plan(int fmt, int M, int N, int K, int &seg_split) {
+    (void)M;
+    const int codes = fmt == FMT_INT2 ? 64 : 32;
+    const int nseg = K / codes;
+    LaneShape sh;
+    seg_split = nseg;
+    if (!pick_shape(nseg, sh)) return 1;
+    long rg = ((long)N + 64 / sh.RL - 1) / (64 / sh.RL);
+    int best = 1;
+    for (int S = 2; S <= 16 && rg < kSplitTargetRowGroups; S *= 2) {
+        const int ss = (nseg + S - 1) / S;
+        if (ss < 4 || !pick_shape(ss, sh)) break;
+        const int seff = (nseg + ss - 1) / ss;
+        best = seff;
+        seg_split = ss;
+        rg = ((long)N + 64 / sh.RL - 1) / (64 / sh.RL) * seff;
+    }
+    if (best == 1) seg_split = nseg;
+    return best;
+}
+
+size_t splitk_workspace_bytes(int fmt, int M, int N, int K) {
+    int ss;
+    const int S = splitk_plan(fmt, M, N, K, ss);
+    return S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_splitk_matvec(const MatvecArgs &a0, void *ws, hipStream_t st) {
+    MatvecArgs a = a0;
+    int ss;
+    const int S = splitk_plan(a.fmt, a.M, a.N, a.K, ss);
+    if (S == 1) return launch_fo_matvec(a, st);
+    a.seg_split = ss;
+    a.splits = S;
+    a.part = reinterpret_cast<float *>(ws);
+    hipError_t e = launch_fo_matvec(a, st);
+    if (e != hipSuccess) return e;
+    const size_t total = (size_t)a.M * a.N;
+    size_t g = (total + 255) / 256;
+    if (g > 4096) g = 4096;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)g), dim3(256), 0, st, a.part, S, a.M, a.N,
+                       a.fmt == FMT_INT2 ? reinterpret_cast<const uint16_t *>(a.sc) : nullptr, a.y, a.y_dtype);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {

@@ -26,9 +26,20 @@ struct MatvecArgs {
     void *y;            // [M][N]
     int y_dtype;
     int M, N, K;
+    int seg_split = 0;      // segments per K split (0: the whole row)
+    int splits = 1;         // K splits (grid z)
+    float *part = nullptr;  // split partial sums [splits][M][N], or nullptr
 };
 
 hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t stream);
+
+// Split-K (tolerance class): the number of K splits chosen for a shape and
+// the segments per split; 1 split means the fixed-order kernel is used.
+int splitk_plan(int fmt, int M, int N, int K, int &seg_split);
+size_t splitk_workspace_bytes(int fmt, int M, int N, int K);
+// Partial sums of every split into `ws`, then their sum in increasing split
+// order (plus the int2 row scale) into y.
+hipError_t launch_splitk_matvec(const MatvecArgs &a, void *ws, hipStream_t stream);
 
 // Matrix-core MXFP4 GEMM (tolerance class), 32 <= M <= 256.
 hipError_t launch_mxfp4_mfma(const MatvecArgs &a, hipStream_t stream);

@@ -127,3 +127,18 @@ def test_workspace_init_validation():
     assert q._lib.qmv_workspace_init(None, 256, None) == INVALID
     assert q._lib.qmv_workspace_init(P(128), 256, None) == ALIGN
     assert q._lib.qmv_workspace_init(P(256), 6, None) == ALIGN
+
+
+def test_splitk_workspace_size_and_validation():
+    # several K splits for a short-N int2 matvec: [splits][M][N] fp32 partials
+    need = q.workspace_size("int2", 1, 2048, 1536, "splitk")
+    assert need > 0 and need % (2048 * 4) == 0 and need // (2048 * 4) in (2, 4, 8, 16)
+    assert q.workspace_size("int2", 3, 2048, 1536, "splitk") == 3 * need
+    # enough rows for the whole GPU: one split, no workspace (fixed-order kernel)
+    assert q.workspace_size("int2", 1, 70000, 1536, "splitk") == 0
+    assert q.workspace_size("int4", 1, 16384, 4096, "splitk") == 0
+    assert q.workspace_size("int2", 1, 2048, 1536, "fixed") == 0
+    fn = q._lib.qmv_int2
+    assert _mv(fn, M=1, N=2048, K=1536, mode=1) == WS
+    assert _mv(fn, M=1, N=2048, K=1536, mode=1, ws=4096, wsb=need - 4) == WS
+    assert _mv(fn, M=1, N=2048, K=1536, mode=1, ws=4096 + 16, wsb=need) == ALIGN
