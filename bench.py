@@ -35,7 +35,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP32_VALU_FMA_PER_S = 78.6e12 / 2  # binary32 FMA rate without packed math (256 CU x 64 lanes x 2.4 GHz)
-BF16_MFMA_PEAK = 2.5e15
+BF16_MFMA_PEAK = 2.5e15     # dense bf16 matrix-core rate
+MXFP4_MFMA_PEAK = 10.1e15   # dense MXFP4 rate, for comparison only
 COLD_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -147,14 +148,19 @@ def sweep_cases():
     import skinny_gemm_qmv_amd as q
     import synth
 
-    def int2_c1():
-        d = synth.int2_inputs(1, 2048, 1536, workload=1)
-        wb = 2048 * 1536 // 4 + 2048 * 2
-        cp = -(-COLD_BYTES // wb)
-        wq, sc = rotating(dev(d["wq"], "u32"), cp), rotating(dev(d["scale"], "f16"), cp)
-        x = dev(d["x"], "f16")
-        y = torch.empty((1, 2048), device="cuda")
-        return (lambda i: (lambda: q.qmv_int2(wq[i % cp], sc[i % cp], x, y=y))), wb + 3072 + 8192, 2 * 2048 * 1536, "hbm"
+    def int2_c1(mode="fixed"):
+        def b():
+            d = synth.int2_inputs(1, 2048, 1536, workload=1)
+            wb = 2048 * 1536 // 4 + 2048 * 2
+            cp = -(-COLD_BYTES // wb)
+            wq, sc = rotating(dev(d["wq"], "u32"), cp), rotating(dev(d["scale"], "f16"), cp)
+            x = dev(d["x"], "f16")
+            y = torch.empty((1, 2048), device="cuda")
+            need = q.workspace_size("int2", 1, 2048, 1536, mode)
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+            return (lambda i: (lambda: q.qmv_int2(wq[i % cp], sc[i % cp], x, y=y, mode=mode, workspace=ws))), \
+                wb + 3072 + 8192, 2 * 2048 * 1536, "hbm"
+        return b
 
     def int4_m(M):
         def b():
@@ -193,7 +199,7 @@ def sweep_cases():
                 2 * M * 262144 * 1536, "hbm" if M == 1 else "alu"
         return b
 
-    def mxfp4_m(M):
+    def mxfp4_m(M, mode="fixed"):
         def b():
             d = synth.mxfp4_inputs(M, 21504, 5376, workload=5)
             wb = 21504 * 5376 // 2 + 21504 * 168
@@ -201,12 +207,19 @@ def sweep_cases():
             wq, e = rotating(dev(d["wq"], "u8"), cp), rotating(dev(d["e8m0"], "u8"), cp)
             x = dev(d["x"], "bf16")
             y = torch.empty((M, 21504), device="cuda")
-            return (lambda i: (lambda: q.qmm_mxfp4(wq[i % cp], e[i % cp], x, y=y))), \
-                wb + M * 5376 * 2 + M * 21504 * 4, 2 * M * 21504 * 5376, "hbm" if M == 1 else "alu"
+            if mode == "mfma":
+                # the bf16 matrix-core rate binds once the arithmetic intensity
+                # (2M flops per 0.53 weight bytes) passes its ridge (~312 flop/B)
+                bound = "hbm" if M <= 64 else "mfma"
+            else:
+                bound = "hbm" if M == 1 else "alu"
+            return (lambda i: (lambda: q.qmm_mxfp4(wq[i % cp], e[i % cp], x, y=y, mode=mode))), \
+                wb + M * 5376 * 2 + M * 21504 * 4, 2 * M * 21504 * 5376, bound
         return b
 
     return [
-        ("int2 N=2048 K=1536 M=1", int2_c1),
+        ("int2 N=2048 K=1536 M=1", int2_c1()),
+        ("int2 N=2048 K=1536 M=1 split-K", int2_c1("splitk")),
         ("int4 N=16384 K=4096 M=4", int4_m(4)),
         ("int4 N=16384 K=4096 M=8", int4_m(8)),
         ("int4 N=16384 K=4096 M=16", int4_m(16)),
@@ -217,6 +230,8 @@ def sweep_cases():
         ("mxfp4 N=21504 K=5376 M=16", mxfp4_m(16)),
         ("mxfp4 N=21504 K=5376 M=64", mxfp4_m(64)),
         ("mxfp4 N=21504 K=5376 M=256", mxfp4_m(256)),
+        ("mxfp4 N=21504 K=5376 M=64 matrix cores", mxfp4_m(64, "mfma")),
+        ("mxfp4 N=21504 K=5376 M=256 matrix cores", mxfp4_m(256, "mfma")),
     ]
 
 
@@ -224,6 +239,8 @@ def roof_fraction(bound, nbytes, flops, sec):
     gbs = effective_gbps(nbytes, sec)
     if bound == "hbm":
         return gbs / HBM_PEAK_GBS
+    if bound == "mfma":
+        return flops / sec / BF16_MFMA_PEAK
     # fixed-order arithmetic: one binary32 FMA per (code, activation column)
     return (flops / 2 / sec) / FP32_VALU_FMA_PER_S
 
@@ -300,10 +317,14 @@ def main():
         for label, b in sweep_cases():
             mk, nb, fl, bound = b()
             s = run_case(mk, max(20, args.steps // 10), max(5, args.warmup // 10))
-            extra.append({"workload": label, "us_per_call": round(s * 1e6, 3),
-                          "GB/s": round(effective_gbps(nb, s), 1),
-                          "TFLOP/s": round(fl / s / 1e12, 3), "bound": bound,
-                          "roofline_frac": round(roof_fraction(bound, nb, fl, s), 4)})
+            rec = {"workload": label, "us_per_call": round(s * 1e6, 3),
+                   "GB/s": round(effective_gbps(nb, s), 1),
+                   "TFLOP/s": round(fl / s / 1e12, 3), "bound": bound,
+                   "roofline_frac": round(roof_fraction(bound, nb, fl, s), 4)}
+            if "matrix cores" in label:
+                rec["frac_of_bf16_mfma_peak"] = round(fl / s / BF16_MFMA_PEAK, 4)
+                rec["frac_of_mxfp4_mfma_peak"] = round(fl / s / MXFP4_MFMA_PEAK, 4)
+            extra.append(rec)
             del mk
             torch.cuda.empty_cache()
 
