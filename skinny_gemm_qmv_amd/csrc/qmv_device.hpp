@@ -335,6 +335,32 @@ __device__ __forceinline__ void segment_sums_rows(const u4_t (&w)[R], const Deco
     }
 }
 
+// The value of lane l + S for lanes l whose group of 2S lanes starts at a
+// multiple of 2S (other lanes get values that the tree never reads).
+// S <= 8: a DPP row shift inside the 16-lane row (one VALU instruction,
+// folded into the add); S = 16, 32 cross 16-lane rows and go through
+// ds_bpermute.
+template <int S>
+__device__ __forceinline__ float lane_down(float r) {
+    if constexpr (S >= 16) {
+        return __shfl_down(r, S, 64);
+    } else {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, r), 0x100 + S, 0xF, 0xF, true));
+    }
+}
+
+// One cross-lane tree level of distance S in groups of RL lanes (levels with
+// S >= RL do not exist; levels above the padded width s0 are skipped).
+template <int RL, int S>
+__device__ __forceinline__ void lane_level(float &r, int s0) {
+    if constexpr (S < RL) {
+        const float o = lane_down<S>(r);
+        if (S <= s0) r = r + o;
+    }
+}
+
+
 // Fixed-order tree over the segment values of one row.  Lane q of a group
 // of RL lanes holds the segments j = q + RL*a in v[a] (+0 beyond the row's
 // segment count).  The halving tree over P2 entries
@@ -354,12 +380,14 @@ __device__ __forceinline__ float fo_tree(float (&v)[NIP], int P2) {
         }
     }
     float r = v[0];
-    const int s0 = (P2 < RL ? P2 : RL) / 2;
-#pragma unroll
-    for (int s = RL / 2; s >= 1; s >>= 1) {
-        const float o = __shfl_down(r, s, RL);
-        if (s <= s0) r = r + o;
-    }
+    // rows shorter than a lane group (P2 < RL) skip the levels above P2/2
+    const int s0 = P2 >= RL ? RL / 2 : P2 / 2;
+    lane_level<RL, 32>(r, s0);
+    lane_level<RL, 16>(r, s0);
+    lane_level<RL, 8>(r, s0);
+    lane_level<RL, 4>(r, s0);
+    lane_level<RL, 2>(r, s0);
+    lane_level<RL, 1>(r, s0);
     return r;
 }
 

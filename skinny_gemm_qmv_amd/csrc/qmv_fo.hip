@@ -114,9 +114,12 @@ constexpr int ring_depth() {
 #ifndef QMV_ROWS
 #define QMV_ROWS 2
 #endif
+#ifndef QMV_ROWS1
+#define QMV_ROWS1 1
+#endif
 template <int MC, bool XREG>
 constexpr int rows_block() {
-    return (MC > 1 && !XREG) ? QMV_ROWS : 1;
+    return (MC > 1 && !XREG) ? QMV_ROWS : (MC == 1 ? QMV_ROWS1 : 1);
 }
 
 // Raw loaded bits only: converting a scale in the load routine would make
@@ -738,7 +741,7 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
         constexpr bool xreg = xreg_fits<F, NI>();
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, xreg>;
         const size_t lds = (size_t)klen * 2;
-        hipLaunchKernelGGL(k, dim3(gx(k, lds, D), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
+        hipLaunchKernelGGL(k, dim3(gx(k, lds, D * QMV_ROWS1), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
                            a.N, a.K, seg_split, a.part);
     } else if (wide_fits(klen, 1, mc_wide<NI>())) {
         constexpr int MCW = mc_wide<NI>();
