@@ -40,7 +40,7 @@ bool pick_shape(int nseg, LaneShape &s) {
     else if (nseg <= 24) s = {8, 3, 4};
     else if (nseg <= 32) s = {32, 1, 1};
     else if (nseg <= 64) s = {64, 1, 1};
-    else if (nseg <= 128) s = {64, 2, 2};
+    else if (nseg <= 128) s = {32, 4, 4};  // two rows per wave: half the tree and epilogue work per row
     else if (nseg <= 192) s = {64, 3, 4};
     else if (nseg <= 256) s = {64, 4, 4};
     else if (nseg <= 512) s = {64, 8, 8};
@@ -164,7 +164,14 @@ struct FoEngine {
     __amdgpu_buffer_rsrc_t rw[NMAT], rsc[NMAT];
     uint32_t woff, soff;        // offsets of the next unit to load
     uint32_t wstep, sstep;      // bytes between consecutive units of a wave
-    RowSlot<F, NI, NMAT, R> slot[D];
+    // With one activation column a slot is refilled before the unit in it is
+    // computed (D units always in flight), which takes D + 1 slots; the unit
+    // loop is unrolled over all of them so no slot is ever copied.  With
+    // several columns read from LDS the kernel is bound by arithmetic and a
+    // slot is refilled after its unit, keeping registers (and occupancy).
+    static constexpr bool kRefillFirst = XREG || MC == 1;
+    static constexpr int NSLOT = kRefillFirst ? D + 1 : D;
+    RowSlot<F, NI, NMAT, R> slot[NSLOT];
 
     static constexpr int kNT = 2;  // non-temporal: the weights are read once
 
@@ -278,17 +285,14 @@ struct FoEngine {
             const int j = q + RL * i;
             xoff[i] = (j < nseg ? j : nseg - 1) * CODES;
         }
-        for (int base = first; base < total_units; base += D * stride) {
+        for (int base = first; base < total_units; base += NSLOT * stride) {
 #pragma unroll
-            for (int d = 0; d < D; ++d) {
+            for (int d = 0; d < NSLOT; ++d) {
                 const int u = base + d * stride;
-                // With one activation column the wave refills a slot before
-                // computing it (D units always in flight); with several read
-                // from LDS the kernel is bound by arithmetic and two live slots
-                // would cost the registers that set its occupancy.
-                constexpr bool kRefillFirst = XREG || MC == 1;
-                const RowSlot<F, NI, NMAT, R> cur = slot[d];
-                if constexpr (kRefillFirst) load(slot[d]);
+                // slot d holds unit u; refill-first loads unit u + D*stride
+                // into the slot that was computed last
+                if constexpr (kRefillFirst) load(slot[(d + D) % NSLOT]);
+                const RowSlot<F, NI, NMAT, R> &cur = slot[d];
                 if (u < total_units) {  // uniform across the wave
                     if constexpr (XREG) {
                         // keep the register copy of x opaque to loop-invariant
@@ -766,7 +770,7 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
     case 834: return FN<8, 3, 4>(__VA_ARGS__);                              \
     case 3211: return FN<32, 1, 1>(__VA_ARGS__);                            \
     case 6411: return FN<64, 1, 1>(__VA_ARGS__);                            \
-    case 6422: return FN<64, 2, 2>(__VA_ARGS__);                            \
+    case 3244: return FN<32, 4, 4>(__VA_ARGS__);                            \
     case 6434: return FN<64, 3, 4>(__VA_ARGS__);                            \
     case 6444: return FN<64, 4, 4>(__VA_ARGS__);                            \
     case 6488: return FN<64, 8, 8>(__VA_ARGS__);                            \
