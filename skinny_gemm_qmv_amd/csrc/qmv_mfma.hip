@@ -61,10 +61,22 @@ struct ChunkSlot {
 };
 
 // Chunks in flight besides the one being multiplied.
+// Even, so that the loop unrolled over D slots also alternates the two
+// fragment sets.
 template <int WV, int MW>
 constexpr int mfma_depth() {
-    return WV == 4 ? 4 : (MW == 1 ? 3 : 2);
+    return WV == 4 ? 4 : 2;
 }
+
+// Weight fragments of one chunk read back from LDS: the raw MXFP4 dwords of
+// every tile (4 sub-steps each) and their scales.  (A fragments are read per
+// sub-step inside the multiply; holding a second set of them would cost the
+// registers that give two waves per SIMD.)
+template <int NB>
+struct Frags {
+    u4_t braw[NB];
+    float sc[NB];
+};
 
 template <int WV, int MW, int NB>
 __global__ __launch_bounds__(WV * 64) void k_mxfp4_mfma(
@@ -74,7 +86,7 @@ __global__ __launch_bounds__(WV * 64) void k_mxfp4_mfma(
     constexpr int WT = (NB + WV - 1) / WV;  // tile slots loaded by each wave
     __shared__ __align__(16) uint8_t wbuf[2][NB][kWTile];
     __shared__ __align__(16) uint8_t sbuf[2][NB][64];
-    __shared__ __align__(16) uint8_t xpad[WV][MW * 16 * kXRow];
+    __shared__ __align__(16) uint8_t xpad[WV][2][MW * 16 * kXRow];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int lrow = lane >> 2, lpc = lane & 3;  // weight load layout
@@ -138,18 +150,18 @@ __global__ __launch_bounds__(WV * 64) void k_mxfp4_mfma(
 #pragma unroll
     for (int d = 0; d < D; ++d) load(slot[d], d);
 
-    uint8_t *xp = xpad[wave];
     const bool active = m0w < M;  // uniform: this wave has activation rows
-    // Chunk c: the wave's weight slots go to buffer c&1 and its activation
-    // rows to its pad, one barrier publishes the weights (every wave has
-    // then also finished chunk c-1, which read the other buffer, and chunk
-    // c-2, the last reader of this one; the pad is private and LDS accesses
-    // of a wave complete in order), the slot is refilled with chunk c+D, and
-    // the tile products are accumulated.
-    auto step = [&](ChunkSlot<WT, MW> &sl, int c) {
-        const ChunkSlot<WT, MW> cur = sl;
+    // Software pipeline over chunks.  Iteration c: publish chunk c+1 (the
+    // wave's weight slots to the shared buffer (c+1)&1, its activation rows
+    // to its pad (c+1)&1), one barrier (every wave has then finished reading
+    // chunk c-1's fragments, the last reads of those buffers), refill the slot
+    // with chunk c+1+D, read chunk c+1's fragments, and multiply chunk c from
+    // the fragments read one iteration earlier -- so the LDS reads of the next
+    // chunk overlap this chunk's matrix work.
+    auto publish = [&](const ChunkSlot<WT, MW> &cur, int c) {
         uint8_t(*wb)[kWTile] = wbuf[c & 1];
         uint8_t(*sb)[64] = sbuf[c & 1];
+        uint8_t *xp = xpad[wave][c & 1];
 #pragma unroll
         for (int s = 0; s < WT; ++s)
             if (sok[s]) {
@@ -162,49 +174,72 @@ __global__ __launch_bounds__(WV * 64) void k_mxfp4_mfma(
             for (int q = 0; q < 4; ++q)
                 *reinterpret_cast<u4_t *>(&xp[(mw * 16 + 4 * q + (lane >> 4)) * kXRow + 16 * (lane & 15)]) =
                     cur.x[mw][q];
-        __syncthreads();
-        load(sl, c + D);  // past the end: out-of-range offsets, no traffic
-        if (active) {
-            u4_t braw[NB];
-            float sc[NB];
+    };
+    auto read_frags = [&](Frags<NB> &f, int c) {
+        uint8_t(*wb)[kWTile] = wbuf[c & 1];
+        uint8_t(*sb)[64] = sbuf[c & 1];
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                braw[i] = *reinterpret_cast<const u4_t *>(&wb[i][r16 * kWRow + 16 * g]);
-                sc[i] = e8m0_to_f32(sb[i][r16 * 4 + g]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf8_t a[MW];
-#pragma unroll
-                for (int mw = 0; mw < MW; ++mw)
-                    a[mw] = __builtin_bit_cast(
-                        bf8_t, *reinterpret_cast<const u4_t *>(&xp[(mw * 16 + r16) * kXRow + 64 * g + 16 * j]));
-#pragma unroll
-                for (int i = 0; i < NB; ++i) {
-                    const uint32_t wd = braw[i][j];
-                    const bf2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 0);
-                    const bf2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 1);
-                    const bf2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 2);
-                    const bf2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[i], 3);
-                    const bf8_t bw = bf8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-#pragma unroll
-                    for (int mw = 0; mw < MW; ++mw)
-                        acc[mw][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mw], bw, acc[mw][i], 0, 0, 0);
-                }
-            }
+        for (int i = 0; i < NB; ++i) {
+            f.braw[i] = *reinterpret_cast<const u4_t *>(&wb[i][r16 * kWRow + 16 * g]);
+            f.sc[i] = e8m0_to_f32(sb[i][r16 * 4 + g]);
         }
     };
-    // Whole groups of D chunks without conditions (loads issued on every
-    // path keep the compiler's count of outstanding loads exact, so each
-    // chunk waits only for its own data), then the remaining < D chunks.
-    int c = 0;
-    for (; c + D <= nchunk; c += D) {
+    // Per sub-step: dequantize every tile's B fragment into its own
+    // registers, then issue the MFMAs.  (Converting into the registers the
+    // previous MFMA is still reading would chain every MFMA behind four
+    // conversions; separate fragments let conversions run under the matrix
+    // work of the previous sub-step.)
+    auto multiply = [&](const Frags<NB> &f, int c) {
+        const uint8_t *xp = xpad[wave][c & 1];
+        // all four sub-steps' A fragments first: one LDS latency per chunk
+        u4_t af[4][MW];
 #pragma unroll
-        for (int d = 0; d < D; ++d) step(slot[d], c + d);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int mw = 0; mw < MW; ++mw)
+                af[j][mw] = *reinterpret_cast<const u4_t *>(&xp[(mw * 16 + r16) * kXRow + 64 * g + 16 * j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u4_t(&a)[MW] = af[j];
+            bf8_t bw[NB];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const uint32_t wd = f.braw[i][j];
+                const bf2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, f.sc[i], 0);
+                const bf2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, f.sc[i], 1);
+                const bf2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, f.sc[i], 2);
+                const bf2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, f.sc[i], 3);
+                bw[i] = bf8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            }
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int mw = 0; mw < MW; ++mw)
+                    acc[mw][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a[mw]), bw[i],
+                                                                        acc[mw][i], 0, 0, 0);
+        }
+    };
+
+    Frags<NB> fr[2];
+    publish(slot[0], 0);
+    __syncthreads();
+    load(slot[0], D);
+    read_frags(fr[0], 0);
+    // Every iteration issues the same loads and LDS traffic (chunks past the
+    // end read nothing and are never multiplied), so the compiler's count of
+    // outstanding loads stays exact; the loop runs over whole groups of D.
+    for (int c0 = 0; c0 < nchunk; c0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int c = c0 + d;
+            ChunkSlot<WT, MW> &nxt = slot[(d + 1) % D];  // holds chunk c+1
+            publish(nxt, c + 1);
+            __syncthreads();
+            load(nxt, c + 1 + D);
+            read_frags(fr[(d + 1) & 1], c + 1);
+            if (active && c < nchunk) multiply(fr[d & 1], c);
+        }
     }
-#pragma unroll
-    for (int d = 0; d < D - 1; ++d)
-        if (c + d < nchunk) step(slot[d], c + d);
 
     // D[i][j] of a 16x16 tile: lane l holds rows 4(l/16) .. 4(l/16)+3 of column l%16.
     if (!active) return;
