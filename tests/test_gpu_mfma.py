@@ -109,3 +109,17 @@ def test_mfma_rejects_narrow_batches():
     d = synth.mxfp4_inputs(31, 64, 64, salt=1)
     with pytest.raises(q.QmvError):
         gpu_mfma(d)
+
+
+def test_mfma_exact_on_integer_inputs():
+    """Integer activations in [-8, 8] and block scales 2^0 / 2^1: every product
+    and every partial sum is exact in fp32 (multiples of 0.5 below 2^20), so
+    the matrix cores must give the exact result bit for bit."""
+    g = np.random.default_rng(7)
+    M, N, K = 96, 1000, 5376
+    d = dict(wq=synth.raw_bytes(g, (N, K // 2)),
+             e8m0=(127 + g.integers(0, 2, (N, K // 32))).astype(np.uint8),
+             x=synth.bf16_bits(g.integers(-8, 9, (M, K)).astype(np.float64)))
+    y = gpu_mfma(d).cpu().numpy().astype(np.float64)
+    exact, _ = oracle.ref64_mxfp4(d["wq"], d["e8m0"], d["x"])
+    assert np.array_equal(y, exact)

@@ -106,3 +106,31 @@ def test_splitk_caller_workspace_reused():
         torch.cuda.synchronize()
         fo, _, _ = references("int2", d)
         assert rel_l2(y.cpu().numpy(), fo) <= TOL
+
+
+def _integer_inputs(fmt, M, N, K, seed):
+    """Integer activations in [-8, 8] and power-of-two scales chosen so that
+    every partial sum in any order is exactly representable in fp32 (the
+    bound on |sum| over the resolution of the terms stays below 2^24)."""
+    g = np.random.default_rng(seed)
+    if fmt == "mxfp4":
+        x = synth.bf16_bits(g.integers(-8, 9, (M, K)).astype(np.float64))
+        return dict(wq=synth.raw_bytes(g, (N, K // 2)), x=x,
+                    e8m0=(127 + g.integers(0, 2, (N, K // 32))).astype(np.uint8))
+    x = synth.f16_bits(g.integers(-8, 9, (M, K)).astype(np.float64))
+    if fmt == "int2":
+        return dict(wq=synth.raw_words(g, (N, K // 16)), x=x,
+                    scale=synth.f16_bits(np.ldexp(1.0, g.integers(-4, 3, N))))
+    return dict(wq=synth.raw_words(g, (N, K // 8)), x=x,
+                scales=synth.f16_bits(np.ldexp(1.0, g.integers(-2, 2, (N, K // 32)))))
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("int2", 2, 1000, 4096), ("int4", 3, 777, 4096), ("mxfp4", 5, 600, 5376)])
+def test_splitk_exact_on_integer_inputs(fmt, M, N, K):
+    """With every partial sum exact, split-K must equal the exact result bit
+    for bit whatever its summation order."""
+    d = _integer_inputs(fmt, M, N, K, seed={"int2": 11, "int4": 12, "mxfp4": 13}[fmt])
+    assert q.workspace_size(fmt, M, N, K, "splitk") > 0  # really split
+    y = run(fmt, d, "splitk")
+    _, exact, _ = references(fmt, d)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), exact)
