@@ -48,6 +48,24 @@ bool pick_shape(int nseg, LaneShape &s) {
     return true;
 }
 
+// Few rows: when N fills fewer than ~4 row groups per SIMD, spread a row
+// over more lanes (fewer rows per wave, more waves) as long as at least half
+// of the row's lanes hold a segment.  The order of the sums does not depend
+// on the layout.
+constexpr long kFewRowGroups = 4096;
+
+bool pick_shape_rows(int nseg, long N, LaneShape &s) {
+    if (!pick_shape(nseg, s)) return false;
+    static const LaneShape wider[] = {{16, 1, 1}, {32, 1, 1}, {64, 1, 1}};
+    for (const LaneShape &w : wider) {
+        const long rg = (N + 64 / s.RL - 1) / (64 / s.RL);
+        if (rg >= kFewRowGroups) break;
+        if (w.RL <= s.RL || w.RL * w.NI < nseg || w.RL > 2 * nseg) continue;
+        s = w;
+    }
+    return true;
+}
+
 static inline int pow2_ceil(int n) {
     int p = 1;
     while (p < n) p <<= 1;
@@ -516,6 +534,95 @@ __device__ void rmsnorm_prologue(const uint16_t *__restrict__ x, const uint16_t 
     __syncthreads();
 }
 
+// The same prologue for one activation row per workgroup (M = 1 decode),
+// shortened to one global round trip and one barrier before normalising:
+// every thread loads its gamma vectors at once; lane j of wave 0 loads the
+// x and residual values of segments j, j+64, ... itself, forms h, writes it
+// to LDS (and residual_out) and sums the squares from registers in the
+// fixed order; the tree and inv follow in the same wave.
+__device__ void rmsnorm_prologue1(const uint16_t *__restrict__ x, const uint16_t *__restrict__ res,
+                                  const uint16_t *__restrict__ gamma, uint16_t *res_out, float eps, int K,
+                                  int m, uint16_t *xs, float *inv_s) {
+    constexpr int kGv = 1;  // gamma vectors kept in registers per thread (all of them for K <= 2048)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nvec = K / 8;
+    u4_t gv[kGv];
+#pragma unroll
+    for (int i = 0; i < kGv; ++i) {
+        const int v = tid + i * kBlock;
+        gv[i] = v < nvec ? *reinterpret_cast<const u4_t *>(gamma + 8 * v) : u4_t{0u, 0u, 0u, 0u};
+    }
+    const size_t row = (size_t)m * K;
+    if (wave == 0) {
+        const int nseg = K / 64;
+        int P2 = 1;
+        while (P2 < nseg) P2 <<= 1;
+        constexpr int NIPP = 4;  // K <= 16384: at most 256 segments = 64 lanes x 4
+        float v[NIPP];
+#pragma unroll
+        for (int a = 0; a < NIPP; ++a) {
+            const int j = lane + 64 * a;
+            float t = 0.0f;
+            if (j < nseg) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                u4_t xv[4], rv[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    xv[q] = *reinterpret_cast<const u4_t *>(x + row + 64 * j + 32 * half + 8 * q);
+                    rv[q] = *reinterpret_cast<const u4_t *>(res + row + 64 * j + 32 * half + 8 * q);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u4_t hv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)  // h = fp16(x + r), one rounding per element
+                        hv[e] = __builtin_bit_cast(uint32_t, u2h2(xv[q][e]) + u2h2(rv[q][e]));
+                    *reinterpret_cast<u4_t *>(xs + 64 * j + 32 * half + 8 * q) = hv;
+                    if (res_out != nullptr && blockIdx.x == 0)
+                        *reinterpret_cast<u4_t *>(res_out + row + 64 * j + 32 * half + 8 * q) = hv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const h2_t hh = u2h2(hv[e]);
+                        const float h0 = (float)hh.x, h1 = (float)hh.y;
+                        t = t + h0 * h0;  // squares exact in fp32; k order
+                        t = t + h1 * h1;
+                    }
+                }
+                }
+            }
+            v[a] = t;
+        }
+        const float ss = fo_tree<64, NIPP>(v, P2);
+        if (lane == 0) {
+            const float ms = ss / (float)K;
+            const float r = ms + eps;
+            const float root = __builtin_sqrtf(r);
+            inv_s[0] = 1.0f / root;
+        }
+    }
+    __syncthreads();
+    const float inv = inv_s[0];
+    for (int i = 0; i * kBlock < nvec; ++i) {
+        const int v = tid + i * kBlock;
+        if (v >= nvec) break;
+        const u4_t g = i < kGv ? gv[i < kGv ? i : 0] : *reinterpret_cast<const u4_t *>(gamma + 8 * v);
+        const u4_t hv = *reinterpret_cast<const u4_t *>(xs + 8 * v);
+        u4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const h2_t hh = u2h2(hv[e]), gg = u2h2(g[e]);
+            const float a0 = (float)hh.x * inv, a1 = (float)hh.y * inv;
+            const float b0 = a0 * (float)gg.x, b1 = a1 * (float)gg.y;
+            const uint32_t lo = __builtin_bit_cast(uint16_t, to_f16(b0));
+            const uint32_t hi = __builtin_bit_cast(uint16_t, to_f16(b1));
+            o[e] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u4_t *>(xs + 8 * v) = o;
+    }
+    __syncthreads();
+}
+
 template <int MC>
 struct GateUpEpi {
     uint16_t *out;
@@ -554,7 +661,10 @@ __global__ __launch_bounds__(kBlock) void k_fo_gateup(
     const void *const s2[2] = {s_gate, s_up};
     FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 2, ring_depth<NI, 2>(), rows_block<MC, XREG>()> eng(w2, s2, N, K);
     eng.prefetch();
-    rmsnorm_prologue<MC>(x, residual, gamma, residual_out, eps, M, K, m0, xs, xs, inv_s);
+    if constexpr (MC == 1)
+        rmsnorm_prologue1(x, residual, gamma, residual_out, eps, K, m0, xs, inv_s);
+    else
+        rmsnorm_prologue<MC>(x, residual, gamma, residual_out, eps, M, K, m0, xs, xs, inv_s);
     GateUpEpi<MC> epi{out, M, N, m0};
     eng.run(xs, epi);
 }
@@ -787,7 +897,8 @@ static hipError_t mv_mxfp4(const MatvecArgs &a, hipStream_t st) { return fo_matv
 hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t st) {
     const int codes = a.fmt == FMT_INT2 ? 64 : 32;
     LaneShape sh;
-    if (!pick_shape(a.seg_split > 0 ? a.seg_split : a.K / codes, sh)) return hipErrorInvalidValue;
+    if (!pick_shape_rows(a.seg_split > 0 ? a.seg_split : a.K / codes, (long)a.N * (a.splits > 0 ? a.splits : 1), sh))
+        return hipErrorInvalidValue;
     if (a.fmt == FMT_INT2) { QMV_SHAPE_SWITCH(mv_int2, a, st) }
     if (a.fmt == FMT_INT4) { QMV_SHAPE_SWITCH(mv_int4, a, st) }
     QMV_SHAPE_SWITCH(mv_mxfp4, a, st)
@@ -823,7 +934,7 @@ static hipError_t gu_shape(const GateUpArgs &a, hipStream_t st) {
 
 hipError_t launch_fo_gateup(const GateUpArgs &a, hipStream_t st) {
     LaneShape sh;
-    if (!pick_shape(a.K / 64, sh)) return hipErrorInvalidValue;
+    if (!pick_shape_rows(a.K / 64, a.N, sh)) return hipErrorInvalidValue;
     QMV_SHAPE_SWITCH(gu_shape, a, st)
 }
 
@@ -870,7 +981,7 @@ static hipError_t am_shape(const ArgmaxArgs &a, hipStream_t st) {
 
 hipError_t launch_fo_argmax(const ArgmaxArgs &a, hipStream_t st) {
     LaneShape sh;
-    if (!pick_shape(a.K / 64, sh)) return hipErrorInvalidValue;
+    if (!pick_shape_rows(a.K / 64, a.N, sh)) return hipErrorInvalidValue;
     QMV_SHAPE_SWITCH(am_shape, a, st)
 }
 
