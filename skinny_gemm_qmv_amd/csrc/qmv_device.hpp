@@ -117,6 +117,24 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return u2f((e << 23) | special);
 }
 
+// v_fma_mix_f32 with two fp16 sources taken from halves of packed
+// registers (AH / BH = 1 selects the high half) and an fp32 addend:
+// acc = acc (+) a*b with one rounding.  fp16 x fp16 products are exact in
+// fp32, so this is the fixed-order step.  Written as an instruction so that
+// the compiler keeps the operands in fp16 (it would otherwise widen a shared
+// operand once and hold the fp32 copies in registers).
+template <int AH, int BH>
+__device__ __forceinline__ void mix_mac(float &acc, uint32_t a2, uint32_t b2) {
+    if constexpr (AH == 0 && BH == 0)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+    else if constexpr (AH == 1 && BH == 0)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+    else if constexpr (AH == 0 && BH == 1)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
+}
+
 // Inner step for the NS segments a lane holds in one row group, for MC
 // activation columns:
 //   t[a][m] = t[a][m] (+) value_k * x[m][k]   for k ascending over segment a.
@@ -145,12 +163,17 @@ __device__ __forceinline__ void segment_sums(const u4_t (&w)[NS], const DecodeCo
                 for (int i = 0; i < 8; ++i) {
 #pragma unroll
                     for (int a = 0; a < NS; ++a) {
-                        const _Float16 cv = half ? c[a][i].y : c[a][i].x;
+                        const uint32_t cp = __builtin_bit_cast(uint32_t, c[a][i]);
 #pragma unroll
                         for (int m = 0; m < MC; ++m) {
-                            const h2_t xp = u2h2(xa[a][m][i >> 1]);
-                            const _Float16 xv = (i & 1) ? xp.y : xp.x;
-                            t[a][m] = __builtin_fmaf((float)cv, (float)xv, t[a][m]);  // exact product
+                            const uint32_t xp = xa[a][m][i >> 1];
+                            if (half) {
+                                if (i & 1) mix_mac<1, 1>(t[a][m], cp, xp);
+                                else mix_mac<1, 0>(t[a][m], cp, xp);
+                            } else {
+                                if (i & 1) mix_mac<0, 1>(t[a][m], cp, xp);
+                                else mix_mac<0, 0>(t[a][m], cp, xp);
+                            }
                         }
                     }
                 }
@@ -168,12 +191,19 @@ __device__ __forceinline__ void segment_sums(const u4_t (&w)[NS], const DecodeCo
             for (int i = 0; i < 8; ++i) {
 #pragma unroll
                 for (int a = 0; a < NS; ++a) {
-                    const _Float16 cv = (i < 4) ? c[a][i].x : c[a][i - 4].y;
+                    // code i of the word: low half of pair i (i < 4) or high
+                    // half of pair i - 4
+                    const uint32_t cp = __builtin_bit_cast(uint32_t, c[a][i & 3]);
 #pragma unroll
                     for (int m = 0; m < MC; ++m) {
-                        const h2_t xp = u2h2(xa[a][m][i >> 1]);
-                        const _Float16 xv = (i & 1) ? xp.y : xp.x;
-                        t[a][m] = __builtin_fmaf((float)cv, (float)xv, t[a][m]);
+                        const uint32_t xp = xa[a][m][i >> 1];
+                        if (i >= 4) {
+                            if (i & 1) mix_mac<1, 1>(t[a][m], cp, xp);
+                            else mix_mac<1, 0>(t[a][m], cp, xp);
+                        } else {
+                            if (i & 1) mix_mac<0, 1>(t[a][m], cp, xp);
+                            else mix_mac<0, 0>(t[a][m], cp, xp);
+                        }
                     }
                 }
             }
@@ -208,23 +238,6 @@ __device__ __forceinline__ void segment_sums(const u4_t (&w)[NS], const DecodeCo
     }
 }
 
-// v_fma_mix_f32 with two fp16 sources taken from halves of packed
-// registers (AH / BH = 1 selects the high half) and an fp32 addend:
-// acc = acc (+) a*b with one rounding.  fp16 x fp16 products are exact in
-// fp32, so this is the fixed-order step.  Written as an instruction so that
-// the compiler keeps the operands in fp16 (it would otherwise widen a shared
-// operand once and hold the fp32 copies in registers).
-template <int AH, int BH>
-__device__ __forceinline__ void mix_mac(float &acc, uint32_t a2, uint32_t b2) {
-    if constexpr (AH == 0 && BH == 0)
-        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
-    else if constexpr (AH == 1 && BH == 0)
-        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,0,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
-    else if constexpr (AH == 0 && BH == 1)
-        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
-    else
-        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
-}
 
 // Inner step for one segment of R rows (the same segment index of R
 // different rows) and MC activation columns read from LDS:

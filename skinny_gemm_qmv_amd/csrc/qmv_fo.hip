@@ -157,10 +157,12 @@ __device__ __forceinline__ float seg_scale(uint32_t bits) {
 
 // The FO row engine.  NMAT weight matrices (1, or 2 for gate/up) share the
 // activation chunk.  A wave walks units u = first, first+stride, ...; a unit
-// is R adjacent row groups of RPG rows each.  Loads go through a ring of D
-// slots: the next D units are in flight while one is computed.  prefetch()
-// issues the first D loads and is called before the activations are staged,
-// so staging overlaps the first weight fetches.  For every row group, lane
+// is R adjacent row groups of RPG rows each.  With one activation column and
+// R = 1 the weights stream through a ring of one-segment slots (run_stream);
+// otherwise loads go through a ring of D unit slots: the next D units are in
+// flight while one is computed.  prefetch() issues the first loads and is
+// called before the activations are staged, so staging overlaps the first
+// weight fetches.  For every row group, lane
 // q == 0 of each RL-lane group hands the reduced totals tot[mat][m] (before
 // the int2 row scale) and the row scales rs[mat] to the epilogue.
 //
@@ -189,7 +191,25 @@ struct FoEngine {
     // slot is refilled after its unit, keeping registers (and occupancy).
     static constexpr bool kRefillFirst = XREG || MC == 1;
     static constexpr int NSLOT = kRefillFirst ? D + 1 : D;
-    RowSlot<F, NI, NMAT, R> slot[NSLOT];
+    // One activation column and one row group per unit: the loads stream at
+    // the granularity of one segment (16 bytes per lane, 1 KB per wave).
+    // Segment i of a unit sits in slot i and is refilled with segment i of
+    // the wave's next unit as soon as it has been summed, so about NI
+    // segments are in flight at all times and the refills are spread evenly
+    // over the computation (rather than one unit's worth at a time, which
+    // leaves the memory system idle and then floods it).  A lane with one
+    // segment per unit uses two slots over two units.
+    static constexpr bool kStream = MC == 1 && R == 1;
+    static constexpr int NS = NI >= 2 ? NI : 2;
+    static constexpr int NU = NS / NI;  // units per pass over the slots
+    struct SegSlot {
+        u4_t w[NMAT];
+        uint32_t sb[NMAT];  // int4 / MXFP4 segment scale bits
+        uint32_t rs[NMAT];  // int2 row scale bits (loaded with segment 0)
+    };
+    SegSlot ss[kStream ? NS : 1];
+    int sseg = 0;  // segment index of the next streamed load
+    RowSlot<F, NI, NMAT, R> slot[kStream ? 1 : NSLOT];
 
     static constexpr int kNT = 2;  // non-temporal: the weights are read once
 
@@ -256,9 +276,50 @@ struct FoEngine {
         soff += sstep;
     }
 
-    __device__ __forceinline__ void prefetch() {
+    // Issue the loads of segment i of the unit at (woff, soff) into `s`;
+    // after the last segment the offsets move to the wave's next unit.
+    __device__ __forceinline__ void load_seg(SegSlot &s, int i) {
+        constexpr uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);
 #pragma unroll
-        for (int d = 0; d < D; ++d) load(slot[d]);
+        for (int t = 0; t < NMAT; ++t) {
+            if constexpr (F == FMT_INT2)
+                if (i == 0) s.rs[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff, 0, 0);
+            s.w[t] = __builtin_bit_cast(u4_t,
+                                        __builtin_amdgcn_raw_buffer_load_b128(rw[t], woff + (uint32_t)(i * RL * 16), 0, kNT));
+            if constexpr (F == FMT_INT4)
+                s.sb[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff + (uint32_t)(i * RL) * ssz, 0, 0);
+            else if constexpr (F == FMT_MXFP4)
+                s.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(rsc[t], soff + (uint32_t)(i * RL) * ssz, 0, 0);
+        }
+        if (i == NI - 1) {
+            woff += wstep;
+            soff += sstep;
+        }
+    }
+
+    __device__ __forceinline__ void prefetch() {
+        if constexpr (kStream) {
+#pragma unroll
+            for (int g = 0; g < NS; ++g) load_seg(ss[g], g % NI);
+        } else {
+#pragma unroll
+            for (int d = 0; d < D; ++d) load(slot[d]);
+        }
+    }
+
+    // The scaled sum of one segment (the int2 row scale comes at the end).
+    __device__ __forceinline__ float scaled(float t, uint32_t sbits) const {
+        if constexpr (F == FMT_INT2) return t;
+        else if constexpr (F == FMT_INT4) return seg_scale<F>(sbits) * t;
+        else return t * seg_scale<F>(sbits);
+    }
+
+    // Pad the scaled segment sums past the row end (+0), then reduce.
+    __device__ __forceinline__ float reduce_scaled(const float (&val)[NI]) const {
+        float v[NIP];
+#pragma unroll
+        for (int a = 0; a < NIP; ++a) v[a] = (a < NI && q + RL * a < nseg) ? val[a] : 0.0f;
+        return fo_tree<RL, NIP>(v, P2);
     }
 
     // Scale the segment sums and pad past the row end (+0), then reduce.
@@ -280,7 +341,83 @@ struct FoEngine {
     }
 
     template <class Epi>
+    __device__ __forceinline__ void run_stream(const uint16_t *xs, Epi &epi) {
+        const DecodeConsts kc;
+        u4_t xr[XREG ? NI : 1][XREG ? XV : 1];
+        int xoff[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int j = q + RL * i;
+            xoff[i] = (j < nseg ? j : nseg - 1) * CODES;
+            if constexpr (XREG) {
+#pragma unroll
+                for (int v = 0; v < XV; ++v)
+                    xr[i][v] = (j < nseg) ? *reinterpret_cast<const u4_t *>(xs + j * CODES + 8 * v)
+                                          : u4_t{0u, 0u, 0u, 0u};
+            }
+        }
+        for (int base = first; base < total_units; base += NU * stride) {
+#pragma unroll
+            for (int uu = 0; uu < NU; ++uu) {
+                const int u = base + uu * stride;
+                float val[NMAT][NI];
+                uint32_t rsb[NMAT];
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    SegSlot &s = ss[(uu * NI + i) % NS];
+                    if (u < total_units) {  // uniform across the wave
+                        // keep the activations opaque to loop-invariant code
+                        // motion (see the unit-ring path)
+                        if constexpr (XREG) {
+#pragma unroll
+                            for (int v = 0; v < XV; ++v) asm volatile("" : "+v"(xr[i][v]));
+                        } else {
+                            asm volatile("" : "+v"(xoff[i]));
+                        }
+                        // the NMAT matrices are independent chains over the
+                        // same activations
+                        float a[NMAT][1];
+#pragma unroll
+                        for (int t = 0; t < NMAT; ++t) a[t][0] = 0.0f;
+                        if constexpr (XREG)
+                            segment_sums<F, NMAT, 1>(s.w, kc, [&](int, int, int vv) { return xr[i][vv]; }, a);
+                        else
+                            segment_sums<F, NMAT, 1>(
+                                s.w, kc,
+                                [&](int, int, int vv) {
+                                    return *reinterpret_cast<const u4_t *>(xs + xoff[i] + 8 * vv);
+                                },
+                                a);
+#pragma unroll
+                        for (int t = 0; t < NMAT; ++t) {
+                            val[t][i] = scaled(a[t][0], s.sb[t]);
+                            if (i == 0) rsb[t] = F == FMT_INT2 ? s.rs[t] : 0u;
+                        }
+                    }
+                    // refill with the same segment of the unit NS segments on
+                    // (unconditional: past the end the loads return zeros)
+                    load_seg(s, i);
+                }
+                if (u < total_units) {
+                    float tot[1][NMAT][1];
+                    float rs[NMAT];
+#pragma unroll
+                    for (int t = 0; t < NMAT; ++t) {
+                        tot[0][t][0] = reduce_scaled(val[t]);
+                        rs[t] = half_bits_to_f32((uint16_t)rsb[t]);
+                    }
+                    epi(u * RPG + rsub, q, tot[0], rs);
+                }
+            }
+        }
+    }
+
+    template <class Epi>
     __device__ __forceinline__ void run(const uint16_t *xs, Epi &epi) {
+        if constexpr (kStream) {
+            run_stream(xs, epi);
+            return;
+        }
         const DecodeConsts kc;
         // x slice of this lane: segments q + RL*i (zeros past the row end)
         u4_t xr[XREG ? NI : 1][XREG ? MC : 1][XREG ? XV : 1];
@@ -781,8 +918,11 @@ __global__ void k_fill_zero(uint32_t *p, size_t words) {
 // groups (its ring filled once), but no more than can be resident on the
 // device at once (occupancy x CUs), so every workgroup starts in the first
 // wave of the launch and none waits for a free CU.
+//
+// `per_cu` (if > 0) caps the resident workgroups per CU below what occupancy
+// allows.  A full launch then has the same number of workgroups on every CU.
 template <class Kern>
-static int grid_for(Kern kernel, size_t lds, long N, int RL, int depth) {
+static int grid_for(Kern kernel, size_t lds, long N, int RL, int depth, int per_cu = 0) {
     const int rpg = 64 / RL;
     const long total_rg = ((long)N + rpg - 1) / rpg;
     long g = (total_rg + (long)kWaves * depth - 1) / ((long)kWaves * depth);
@@ -791,11 +931,28 @@ static int grid_for(Kern kernel, size_t lds, long N, int RL, int depth) {
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kBlock, lds) != hipSuccess || occ < 1)
         occ = 1;
+    if (per_cu > 0 && occ > per_cu) occ = per_cu;
     const long cap = (long)occ * cus;
     if (g > cap) g = cap;
     if (kMaxGrid > 0 && g > kMaxGrid) g = kMaxGrid;
     if (g < 1) g = 1;
     return (int)g;
+}
+
+// Workgroups per CU for a one-column (streaming) launch.  A streaming wave
+// keeps about one 1 KB segment per slot and matrix in flight (NI slots, at
+// least two).  Sized so that a CU has about kStreamKB = 12 such segments per
+// SIMD in flight (~48 KB per CU, e.g. three workgroups of waves holding four
+// segments each), which measured fastest on MI355X: more waves put requests
+// to more DRAM rows in flight at once, fewer leave the latency uncovered.
+#ifndef QMV_STREAM_KB
+#define QMV_STREAM_KB 12
+#endif
+template <int NI, int NMAT>
+constexpr int stream_per_cu() {
+    constexpr int kb = (NI >= 2 ? NI : 2) * NMAT;
+    constexpr int w = (QMV_STREAM_KB + kb / 2) / kb;
+    return w < 1 ? 1 : w;
 }
 
 // M = 1 keeps the activation slice in registers (MC = 1); wider M uses
@@ -847,15 +1004,15 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
     const int S = a.splits > 0 ? a.splits : 1;
     const int klen = seg_split * CODES;  // activation values staged per column
     // workgroups along x for one split: sized as if the S splits were S*N rows
-    auto gx = [&](auto k, size_t lds, int depth) {
-        const int g = grid_for(k, lds, (long)a.N * S, RL, depth);
+    auto gx = [&](auto k, size_t lds, int depth, int per_cu = 0) {
+        const int g = grid_for(k, lds, (long)a.N * S, RL, depth, per_cu);
         return (g + S - 1) / S;
     };
     if (a.M == 1) {
         constexpr bool xreg = xreg_fits<F, NI>();
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, xreg>;
         const size_t lds = (size_t)klen * 2;
-        hipLaunchKernelGGL(k, dim3(gx(k, lds, D * QMV_ROWS1), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
+        hipLaunchKernelGGL(k, dim3(gx(k, lds, D * QMV_ROWS1, stream_per_cu<NI, 1>()), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
                            a.N, a.K, seg_split, a.part);
     } else if (wide_fits(klen, 1, mc_wide<NI>())) {
         constexpr int MCW = mc_wide<NI>();
@@ -912,7 +1069,7 @@ static hipError_t gu_shape(const GateUpArgs &a, hipStream_t st) {
         const size_t lds = (size_t)a.K * 2 + 64;
         if (a.M == 1) {
             auto k = k_fo_gateup<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>;
-            hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), 1), dim3(kBlock), lds, st, a.x,
+            hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D, stream_per_cu<NI, 2>()), 1), dim3(kBlock), lds, st, a.x,
                                a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
                                a.s_up, a.out, a.M, a.N, a.K);
         } else {
@@ -963,7 +1120,7 @@ static hipError_t am_shape(const ArgmaxArgs &a, hipStream_t st) {
     if (a.M == 1) {
         auto k = k_fo_argmax<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>;
         const size_t lds = (size_t)a.K * 2;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D), 1), dim3(kBlock), lds, st, a.wq,
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D, stream_per_cu<NI, 1>()), 1), dim3(kBlock), lds, st, a.wq,
                            a.scale, a.x, a.idx, a.maxval, a.logits, a.M, a.N, a.K, keys, counter);
     } else if (mc == 1) {
         auto k = k_fo_argmax<RL, NI, NIP, 1, false>;
