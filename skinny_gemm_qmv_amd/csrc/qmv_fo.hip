@@ -957,18 +957,19 @@ constexpr int stream_per_cu() {
 
 // M = 1 keeps the activation slice in registers (MC = 1); wider M uses
 // chunks of 4 activation rows read from LDS.
-// Activation rows per workgroup for M > 1: 4, or 2 when a lane holds three or
-// more segments (fewer live values per segment keep the kernel out of
-// scratch).
+// Activation rows per workgroup for M > 1: 4, or 2 where four would push
+// the kernel into scratch (eight segments per lane, or the two-matrix gate/up
+// kernel with three or more).  Every chunk of rows streams the whole weight
+// matrix once, so wider chunks mean fewer passes (int4 M=16: 4 instead of 8).
 #ifndef QMV_MCW
 #define QMV_MCW 4
 #endif
-#ifndef QMV_MCW3
-#define QMV_MCW3 2
+#ifndef QMV_MCW_NARROW
+#define QMV_MCW_NARROW 2
 #endif
-template <int NI>
+template <int NI, int NMAT = 1>
 constexpr int mc_wide() {
-    return NI >= 3 ? QMV_MCW3 : QMV_MCW;
+    return (NI >= 8 || (NMAT == 2 && NI >= 3)) ? QMV_MCW_NARROW : QMV_MCW;
 }
 
 // Units (row blocks) per wave aimed at when sizing a launch that reads the
@@ -1064,7 +1065,7 @@ hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t st) {
 template <int RL, int NI, int NIP>
 static hipError_t gu_shape(const GateUpArgs &a, hipStream_t st) {
     constexpr int D = ring_depth<NI, 2>();
-    constexpr int MCW = mc_wide<NI>();
+    constexpr int MCW = mc_wide<NI, 2>();
     if (a.M == 1 || !wide_fits(a.K, 1, MCW)) {
         const size_t lds = (size_t)a.K * 2 + 64;
         if (a.M == 1) {
