@@ -40,7 +40,8 @@
  *    asynchronous: the status reports argument validation and launch errors
  *    only; kernel completion is observed through the stream.
  *  - Inputs must be finite; results for non-finite inputs are unspecified.
- *  - Each packed weight tensor must be smaller than 4 GiB (the kernels use
+ *  - Each packed weight tensor, and M*N*4 bytes for the output of the
+ *    matvec entry points, must be smaller than 4 GiB (the kernels use
  *    32-bit byte offsets); larger ones return QMV_ERR_UNSUPPORTED.
  *  - Calls that share a workspace must not overlap in time (same stream, or
  *    externally ordered).

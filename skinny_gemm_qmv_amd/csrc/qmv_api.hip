@@ -47,6 +47,8 @@ qmv_status check_matvec(const void *wq, const void *sc, const void *x, const voi
     if (!valid_shape(M, N, K, kmul) || !valid_dtype(dt) || !valid_mode(mode))
         return QMV_ERR_INVALID_ARG;
     if (!fits_32bit(N, K, kmul == 64 ? 4 : 2)) return QMV_ERR_UNSUPPORTED;
+    // y (and split-K partials, fp32) are written with 32-bit byte offsets too
+    if ((uint64_t)M * (uint64_t)N * 4u >= (1ull << 32) - (1ull << 16)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(y, dtype_size(dt)))
         return QMV_ERR_ALIGNMENT;
     return QMV_OK;

@@ -428,6 +428,35 @@ __device__ __forceinline__ void store_out(void *y, size_t idx, float v, int dtyp
         reinterpret_cast<__bf16 *>(y)[idx] = to_bf16(v);
 }
 
+// Output stores that every lane of the wave issues, with no divergent
+// branch around them: a lane with nothing to store passes an offset past the
+// end of the buffer, and the hardware drops that store.  Inside a loop that
+// streams weights through a ring of loads, a store under a divergent branch
+// makes the compiler's count of outstanding memory operations inexact, and it
+// then waits for every load in flight at the top of each row.  dtype
+// (uniform): 0 fp32, 1 fp16, 2 bf16; the buffer holds `elems` elements
+// (elems times the element size must stay below 4 GiB).
+constexpr uint32_t kStoreOob = 0xFFFFFFF0u;
+struct OutBuf {
+    __amdgpu_buffer_rsrc_t r;
+    int dtype;
+    __device__ __forceinline__ OutBuf(void *p, uint32_t elems, int dtype_) : dtype(dtype_) {
+        const uint32_t esz = dtype_ == 0 ? 4u : 2u;
+        r = __builtin_amdgcn_make_buffer_rsrc(p, 0, elems * esz, 0x00020000);
+    }
+    __device__ __forceinline__ void put(bool active, uint32_t idx, float v) const {
+        if (dtype == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(f2u(v), r, active ? idx * 4u : kStoreOob, 0, 0);
+        } else if (dtype == 1) {
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, to_f16(v)), r,
+                                                  active ? idx * 2u : kStoreOob, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, to_bf16(v)), r,
+                                                  active ? idx * 2u : kStoreOob, 0, 0);
+        }
+    }
+};
+
 // e^z for z in [-87, 87]: z = n ln2 + r (Cody & Waite: ln2 split into a
 // 15-significant-bit head, exact when multiplied by |n| <= 127, and a tail),
 // e^r by the degree-7 Taylor polynomial with binary32-rounded coefficients

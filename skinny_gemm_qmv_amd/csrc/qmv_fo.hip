@@ -229,7 +229,9 @@ struct FoEngine {
         const int total_rg = (N + RPG - 1) / RPG;
         total_units = (total_rg + R - 1) / R;
         stride = gridDim.x * kWaves;
-        first = blockIdx.x * kWaves + wave;
+        // wave-uniform: read it through a scalar so that the unit loop is a
+        // scalar loop (no exec-masked control flow around the load ring)
+        first = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wave);
         // bytes of scale data per row
         srow = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u * nseg_row : (uint32_t)nseg_row);
         const uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);  // bytes per scale
@@ -362,6 +364,7 @@ struct FoEngine {
                 const int u = base + uu * stride;
                 float val[NMAT][NI];
                 uint32_t rsb[NMAT];
+                float segdep = 0.0f;
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     SegSlot &s = ss[(uu * NI + i) % NS];
@@ -379,6 +382,16 @@ struct FoEngine {
                         float a[NMAT][1];
 #pragma unroll
                         for (int t = 0; t < NMAT; ++t) a[t][0] = 0.0f;
+                        // segment i's words become available only once segment
+                        // i-1 is summed: left free, the scheduler decodes the
+                        // unit's later segments first, and the wave then waits
+                        // for its newest loads at the top of every unit
+                        if (i > 0) {
+#pragma unroll
+                            for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(s.w[t][v]) : "v"(segdep));
+                        }
                         if constexpr (XREG)
                             segment_sums<F, NMAT, 1>(s.w, kc, [&](int, int, int vv) { return xr[i][vv]; }, a);
                         else
@@ -388,6 +401,7 @@ struct FoEngine {
                                     return *reinterpret_cast<const u4_t *>(xs + xoff[i] + 8 * vv);
                                 },
                                 a);
+                        segdep = a[0][0];
 #pragma unroll
                         for (int t = 0; t < NMAT; ++t) {
                             val[t][i] = scaled(a[t][0], s.sb[t]);
@@ -538,23 +552,20 @@ struct FoEngine {
 // before the int2 row scale into part[m][n].
 template <int F, int MC>
 struct StoreEpi {
-    void *y;
-    float *part;
-    int y_dtype, M, N, m0;
+    OutBuf out;    // y, or this split's fp32 partial sums
+    bool partial;  // uniform
+    int M, N, m0;
     __device__ __forceinline__ void operator()(int n, int q, const float (&tot)[1][MC],
                                                const float (&rs)[1]) {
         const float s = rs[0];
-        if (q != 0 || n >= N) return;
+        const bool act = q == 0 && n < N;
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
-            if (m0 + m < M) {
+            if (m0 + m < M) {  // uniform
                 float r = tot[0][m];
-                if (part != nullptr) {
-                    part[(size_t)(m0 + m) * N + n] = r;
-                } else {
-                    if constexpr (F == FMT_INT2) r = s * r;
-                    store_out(y, (size_t)(m0 + m) * N + n, r, y_dtype);
-                }
+                if constexpr (F == FMT_INT2)
+                    if (!partial) r = s * r;
+                out.put(act, (uint32_t)((m0 + m) * N + n), r);
             }
         }
     }
@@ -586,7 +597,9 @@ __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict_
     eng.prefetch();
     xst.store(xz, xs, M, K, klen, m0);
     __syncthreads();
-    StoreEpi<F, MC> epi{y, part == nullptr ? nullptr : part + (size_t)blockIdx.z * M * N, y_dtype, M, N, m0};
+    StoreEpi<F, MC> epi{OutBuf(part == nullptr ? y : static_cast<void *>(part + (size_t)blockIdx.z * M * N),
+                               (uint32_t)M * (uint32_t)N, part == nullptr ? y_dtype : 0),
+                        part != nullptr, M, N, m0};
     eng.run(xs, epi);
 }
 

@@ -75,6 +75,8 @@ def test_matvec_validation(name, kmul):
     assert _mv(fn, wq=24) == ALIGN
     assert _mv(fn, x=40) == ALIGN
     assert _mv(fn, y=18) == ALIGN          # fp32 output needs 4-byte alignment
+    # the output is addressed with 32-bit byte offsets: M*N*4 must stay below 4 GiB
+    assert _mv(fn, M=256, N=1 << 22, K=kmul) == UNSUP
     if name != "qmm_mxfp4":
         assert _mv(fn, mode=2) == UNSUP       # matrix-core mode only for MXFP4
     else:
