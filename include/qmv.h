@@ -40,9 +40,10 @@
  *    asynchronous: the status reports argument validation and launch errors
  *    only; kernel completion is observed through the stream.
  *  - Inputs must be finite; results for non-finite inputs are unspecified.
- *  - Each packed weight tensor, and M*N*4 bytes for the output of the
- *    matvec entry points, must be smaller than 4 GiB (the kernels use
- *    32-bit byte offsets); larger ones return QMV_ERR_UNSUPPORTED.
+ *  - Each packed weight tensor, M*N*4 bytes for the output of the matvec
+ *    entry points and M*N*2 bytes for the fused entry point's output must
+ *    be smaller than 4 GiB (the kernels use 32-bit byte offsets); larger
+ *    ones return QMV_ERR_UNSUPPORTED.
  *  - Calls that share a workspace must not overlap in time (same stream, or
  *    externally ordered).
  *

@@ -158,6 +158,8 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *resid
         return QMV_ERR_INVALID_ARG;
     if (!valid_shape(M, N, K, 64) || !valid_mode(mode) || !(eps >= 0.0f)) return QMV_ERR_INVALID_ARG;
     if (!fits_32bit(N, K, 4)) return QMV_ERR_UNSUPPORTED;
+    // out (fp16 [M][N]) is written with 32-bit byte offsets
+    if ((uint64_t)M * (uint64_t)N * 2u >= (1ull << 32) - (1ull << 16)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(wq_gate, 16) || !aligned(wq_up, 16) ||
         !aligned(gamma, 2) || !aligned(out, 2) || (residual_out && !aligned(residual_out, 2)))
         return QMV_ERR_ALIGNMENT;

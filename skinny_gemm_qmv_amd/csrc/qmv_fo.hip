@@ -690,74 +690,36 @@ __device__ void rmsnorm_prologue(const uint16_t *__restrict__ x, const uint16_t 
 // x and residual values of segments j, j+64, ... itself, forms h, writes it
 // to LDS (and residual_out) and sums the squares from registers in the
 // fixed order; the tree and inv follow in the same wave.
-__device__ void rmsnorm_prologue1(const uint16_t *__restrict__ x, const uint16_t *__restrict__ res,
-                                  const uint16_t *__restrict__ gamma, uint16_t *res_out, float eps, int K,
-                                  int m, uint16_t *xs, float *inv_s) {
-    constexpr int kGv = 1;  // gamma vectors kept in registers per thread (all of them for K <= 2048)
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nvec = K / 8;
-    u4_t gv[kGv];
-#pragma unroll
-    for (int i = 0; i < kGv; ++i) {
-        const int v = tid + i * kBlock;
-        gv[i] = v < nvec ? *reinterpret_cast<const u4_t *>(gamma + 8 * v) : u4_t{0u, 0u, 0u, 0u};
-    }
-    const size_t row = (size_t)m * K;
-    if (wave == 0) {
-        const int nseg = K / 64;
-        int P2 = 1;
-        while (P2 < nseg) P2 <<= 1;
-        constexpr int NIPP = 4;  // K <= 16384: at most 256 segments = 64 lanes x 4
-        float v[NIPP];
-#pragma unroll
-        for (int a = 0; a < NIPP; ++a) {
-            const int j = lane + 64 * a;
-            float t = 0.0f;
-            if (j < nseg) {
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                u4_t xv[4], rv[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    xv[q] = *reinterpret_cast<const u4_t *>(x + row + 64 * j + 32 * half + 8 * q);
-                    rv[q] = *reinterpret_cast<const u4_t *>(res + row + 64 * j + 32 * half + 8 * q);
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    u4_t hv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)  // h = fp16(x + r), one rounding per element
-                        hv[e] = __builtin_bit_cast(uint32_t, u2h2(xv[q][e]) + u2h2(rv[q][e]));
-                    *reinterpret_cast<u4_t *>(xs + 64 * j + 32 * half + 8 * q) = hv;
-                    if (res_out != nullptr && blockIdx.x == 0)
-                        *reinterpret_cast<u4_t *>(res_out + row + 64 * j + 32 * half + 8 * q) = hv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const h2_t hh = u2h2(hv[e]);
-                        const float h0 = (float)hh.x, h1 = (float)hh.y;
-                        t = t + h0 * h0;  // squares exact in fp32; k order
-                        t = t + h1 * h1;
-                    }
-                }
-                }
-            }
-            v[a] = t;
-        }
-        const float ss = fo_tree<64, NIPP>(v, P2);
-        if (lane == 0) {
-            const float ms = ss / (float)K;
-            const float r = ms + eps;
-            const float root = __builtin_sqrtf(r);
-            inv_s[0] = 1.0f / root;
+// One activation row (M = 1), in two phases so that the global loads of x,
+// the residual and gamma are issued before the weight prefetch (vector loads
+// retire in issue order: loaded after the weights, the prologue would wait
+// for them).  load(): every thread takes one 16-byte vector of x, r and
+// gamma (K <= 2048; longer rows load the rest in finish()).  finish():
+// h = fp16(x + r) to LDS (and residual_out from workgroup 0), then wave 0
+// sums the exact squares segment by segment (64 values, k order) and reduces
+// the segment sums with the fixed tree, then every thread normalises its
+// vectors in place: xn = fp16((fl32(h) * inv) * fl32(gamma)).
+struct RmsStage1 {
+    u4_t xv, rv, gv;
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ x, const uint16_t *__restrict__ res,
+                                         const uint16_t *__restrict__ gamma, int K, int m) {
+        const int v = threadIdx.x, nvec = K / 8;
+        const size_t row = (size_t)m * K;
+        xv = rv = gv = u4_t{0u, 0u, 0u, 0u};
+        if (v < nvec) {
+            xv = *reinterpret_cast<const u4_t *>(x + row + 8 * v);
+            rv = *reinterpret_cast<const u4_t *>(res + row + 8 * v);
+            gv = *reinterpret_cast<const u4_t *>(gamma + 8 * v);
         }
     }
-    __syncthreads();
-    const float inv = inv_s[0];
-    for (int i = 0; i * kBlock < nvec; ++i) {
-        const int v = tid + i * kBlock;
-        if (v >= nvec) break;
-        const u4_t g = i < kGv ? gv[i < kGv ? i : 0] : *reinterpret_cast<const u4_t *>(gamma + 8 * v);
-        const u4_t hv = *reinterpret_cast<const u4_t *>(xs + 8 * v);
+    __device__ static u4_t hsum(const u4_t &a, const u4_t &b) {
+        u4_t h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)  // h = fp16(x + r), one rounding per element
+            h[e] = __builtin_bit_cast(uint32_t, u2h2(a[e]) + u2h2(b[e]));
+        return h;
+    }
+    __device__ static u4_t normalise(const u4_t &hv, const u4_t &g, float inv) {
         u4_t o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -768,28 +730,84 @@ __device__ void rmsnorm_prologue1(const uint16_t *__restrict__ x, const uint16_t
             const uint32_t hi = __builtin_bit_cast(uint16_t, to_f16(b1));
             o[e] = lo | (hi << 16);
         }
-        *reinterpret_cast<u4_t *>(xs + 8 * v) = o;
+        return o;
     }
-    __syncthreads();
-}
+    __device__ __forceinline__ void finish(const uint16_t *__restrict__ x, const uint16_t *__restrict__ res,
+                                           const uint16_t *__restrict__ gamma, uint16_t *res_out, float eps,
+                                           int K, int m, uint16_t *xs, float *inv_s) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int nvec = K / 8;
+        const size_t row = (size_t)m * K;
+        const bool write_res = res_out != nullptr && blockIdx.x == 0;
+        for (int v = tid; v < nvec; v += kBlock) {
+            const u4_t h = v == tid ? hsum(xv, rv)
+                                    : hsum(*reinterpret_cast<const u4_t *>(x + row + 8 * v),
+                                           *reinterpret_cast<const u4_t *>(res + row + 8 * v));
+            *reinterpret_cast<u4_t *>(xs + 8 * v) = h;
+            if (write_res) *reinterpret_cast<u4_t *>(res_out + row + 8 * v) = h;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int nseg = K / 64;
+            int P2 = 1;
+            while (P2 < nseg) P2 <<= 1;
+            constexpr int NIPP = 4;  // K <= 16384: at most 256 segments = 64 lanes x 4
+            float sv[NIPP];
+#pragma unroll
+            for (int a = 0; a < NIPP; ++a) {
+                const int j = lane + 64 * a;
+                float t = 0.0f;
+                if (j < nseg) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const u4_t hv = *reinterpret_cast<const u4_t *>(xs + 64 * j + 8 * q);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const h2_t hh = u2h2(hv[e]);
+                            const float h0 = (float)hh.x, h1 = (float)hh.y;
+                            t = t + h0 * h0;  // squares exact in fp32; k order
+                            t = t + h1 * h1;
+                        }
+                    }
+                }
+                sv[a] = t;
+            }
+            const float ss = fo_tree<64, NIPP>(sv, P2);
+            if (lane == 0) {
+                const float ms = ss / (float)K;
+                const float r = ms + eps;
+                const float root = __builtin_sqrtf(r);
+                inv_s[0] = 1.0f / root;
+            }
+        }
+        __syncthreads();
+        const float inv = inv_s[0];
+        for (int v = tid; v < nvec; v += kBlock) {
+            const u4_t g = v == tid ? gv : *reinterpret_cast<const u4_t *>(gamma + 8 * v);
+            const u4_t hv = *reinterpret_cast<const u4_t *>(xs + 8 * v);
+            *reinterpret_cast<u4_t *>(xs + 8 * v) = normalise(hv, g, inv);
+        }
+        __syncthreads();
+    }
+};
 
 template <int MC>
 struct GateUpEpi {
-    uint16_t *out;
+    OutBuf out;  // fp16 [M][N]
     int M, N, m0;
     __device__ __forceinline__ void operator()(int n, int q, const float (&tot)[2][MC],
                                                const float (&rs)[2]) {
         const float sg = rs[0];
         const float su = rs[1];
-        if (q != 0 || n >= N) return;
+        const bool act = q == 0 && n < N;
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
-            if (m0 + m < M) {
+            if (m0 + m < M) {  // uniform
                 const float g = sg * tot[0][m];
                 const float u = su * tot[1][m];
                 const float ge = qmv_gelu(g);
                 const float o = ge * u;
-                out[(size_t)(m0 + m) * N + n] = __builtin_bit_cast(uint16_t, to_f16(o));
+                out.put(act, (uint32_t)((m0 + m) * N + n), o);
             }
         }
     }
@@ -810,12 +828,16 @@ __global__ __launch_bounds__(kBlock) void k_fo_gateup(
                                   reinterpret_cast<const uint8_t *>(wq_up)};
     const void *const s2[2] = {s_gate, s_up};
     FoEngine<FMT_INT2, RL, NI, NIP, MC, XREG, 2, ring_depth<NI, 2>(), rows_block<MC, XREG>()> eng(w2, s2, N, K);
-    eng.prefetch();
-    if constexpr (MC == 1)
-        rmsnorm_prologue1(x, residual, gamma, residual_out, eps, K, m0, xs, inv_s);
-    else
+    if constexpr (MC == 1) {
+        RmsStage1 rs1;
+        rs1.load(x, residual, gamma, K, m0);
+        eng.prefetch();
+        rs1.finish(x, residual, gamma, residual_out, eps, K, m0, xs, inv_s);
+    } else {
+        eng.prefetch();
         rmsnorm_prologue<MC>(x, residual, gamma, residual_out, eps, M, K, m0, xs, xs, inv_s);
-    GateUpEpi<MC> epi{out, M, N, m0};
+    }
+    GateUpEpi<MC> epi{OutBuf(out, (uint32_t)M * (uint32_t)N, 1), M, N, m0};
     eng.run(xs, epi);
 }
 

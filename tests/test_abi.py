@@ -101,6 +101,7 @@ def test_gateup_validation():
     a = list(args); a[0] = P(18)
     assert call(a) == ALIGN
     assert call(args, mode=2) == UNSUP    # matrix-core mode never applies to int2
+    assert call(args, M=256, N=1 << 23) == UNSUP  # fp16 output of M*N*2 >= 4 GiB (32-bit offsets)
 
 
 def test_argmax_validation():
