@@ -67,6 +67,8 @@ def _bind(lib):
         "orc_int2_rmsnorm_gateup_gelu": ([vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp,
                                           i64, i64, i64, i32], None),
         "orc_int2_argmax": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32], None),
+        "orc_int2_rmsnorm_qkv": ([vp, vp, vp, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64,
+                                  vp, vp, vp, i64, i64, i32], None),
         "orc_ref64_int2": ([vp, vp, vp, vp, vp, i64, i64, i64], None),
         "orc_ref64_int4": ([vp, vp, vp, vp, vp, i64, i64, i64], None),
         "orc_ref64_mxfp4": ([vp, vp, vp, vp, vp, i64, i64, i64], None),
@@ -146,6 +148,24 @@ def int2_rmsnorm_gateup_gelu(x, residual, gamma, eps, wq_gate, s_gate, wq_up, s_
                                      _p(wq_gate), _p(s_gate), _p(wq_up), _p(s_up),
                                      _p(out), _p(g), _p(u), M, N, K, threads or default_threads())
     return out, res_out, g, u
+
+
+def int2_rmsnorm_qkv(x, residual, gamma, eps, wq_q, s_q, wq_k, s_k, wq_v, s_v, threads=None, lib=None):
+    """Shared-prologue q/k/v: residual add + RMSNorm on each row, then three int2
+    fixed-order matvecs on the normalised row.  Returns (yq, yk, yv fp32 [M][N_z],
+    residual_out fp16 bits [M][K])."""
+    lib = lib or load()
+    x, residual, gamma = _c(x, np.uint16), _c(residual, np.uint16), _c(gamma, np.uint16)
+    ws = [_c(w, np.uint32) for w in (wq_q, wq_k, wq_v)]
+    ss = [_c(s, np.uint16) for s in (s_q, s_k, s_v)]
+    M, K = x.shape
+    ys = [np.empty((M, w.shape[0]), np.float32) for w in ws]
+    res_out = np.empty((M, K), np.uint16)
+    lib.orc_int2_rmsnorm_qkv(_p(x), _p(residual), _p(res_out), _p(gamma), float(eps),
+                             _p(ws[0]), _p(ss[0]), ws[0].shape[0], _p(ws[1]), _p(ss[1]), ws[1].shape[0],
+                             _p(ws[2]), _p(ss[2]), ws[2].shape[0], _p(ys[0]), _p(ys[1]), _p(ys[2]),
+                             M, K, threads or default_threads())
+    return ys[0], ys[1], ys[2], res_out
 
 
 def int2_argmax(wq, scale, x, threads=None, lib=None):

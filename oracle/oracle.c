@@ -571,6 +571,30 @@ ORC_API void orc_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *res
     free(h); free(xn); free(g); free(u);
 }
 
+/* Shared-prologue q/k/v ([A19] "What moved the needle", dispatch-count
+ * fusion: the residual-add RMSNorm folded into the next matvec's prologue,
+ * and q/k/v in a single dispatch): the prologue above on each activation
+ * row, then three independent int2 FO matvecs on the normalised row.
+ * x, residual: fp16 [M][K]; gamma fp16 [K]; residual_out fp16 [M][K] or NULL;
+ * wq_z [N_z][K/16], s_z fp16 [N_z]; y_z fp32 [M][N_z] for z = q, k, v. */
+ORC_API void orc_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uint16_t *residual_out,
+                                  const uint16_t *gamma, float eps,
+                                  const uint32_t *wq_q, const uint16_t *s_q, int64_t Nq,
+                                  const uint32_t *wq_k, const uint16_t *s_k, int64_t Nk,
+                                  const uint32_t *wq_v, const uint16_t *s_v, int64_t Nv,
+                                  float *yq, float *yk, float *yv, int64_t M, int64_t K, int nthreads)
+{
+    uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(M * K));
+    uint16_t *xn = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(M * K));
+    for (int64_t m = 0; m < M; ++m)
+        orc_rmsnorm_prologue(x + m * K, residual + m * K, gamma, eps, K, h + m * K, xn + m * K);
+    orc_qmv_int2(wq_q, s_q, xn, yq, M, Nq, K, nthreads);
+    orc_qmv_int2(wq_k, s_k, xn, yk, M, Nk, K, nthreads);
+    orc_qmv_int2(wq_v, s_v, xn, yv, M, Nv, K, nthreads);
+    if (residual_out) memcpy(residual_out, h, sizeof(uint16_t) * (size_t)(M * K));
+    free(h); free(xn);
+}
+
 /* ------------------------------------------------------------------------ */
 /* lm_head: int2 FO logits + argmax, first maximum wins ([A19] parked levers) */
 /* ------------------------------------------------------------------------ */

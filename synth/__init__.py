@@ -91,6 +91,22 @@ def fused_inputs(M, N, K, workload=3, salt=0):
                 wq_gate=wq_gate, s_gate=s_gate, wq_up=wq_up, s_up=s_up)
 
 
+def qkv_inputs(M, Nq, Nk, Nv, K, workload=6, salt=0):
+    """x, residual fp16 [M][K] ~N(0,1); gamma fp16 [K] ~N(1,0.1); q/k/v int2 [N_z][K/16]
+    with fp16 per-row scales ~U(0.01,0.05); eps = 1e-6 (the fused workload's recipe with
+    three output matrices)."""
+    g = rng(workload, M, salt)
+    out = {}
+    for z, n in (("q", Nq), ("k", Nk), ("v", Nv)):
+        out["wq_" + z] = raw_words(g, (n, K // 16))
+        out["s_" + z] = f16_bits(g.uniform(0.01, 0.05, size=n))
+    out["x"] = f16_bits(g.standard_normal((M, K)))
+    out["residual"] = f16_bits(g.standard_normal((M, K)))
+    out["gamma"] = f16_bits(g.normal(1.0, 0.1, size=K))
+    out["eps"] = 1e-6
+    return out
+
+
 def argmax_inputs(M, N, K, workload=4, salt=0):
     return int2_inputs(M, N, K, workload=workload, salt=salt)
 

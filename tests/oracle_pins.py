@@ -403,6 +403,41 @@ def check_fused_composition(lib):
         assert np.max(np.abs(o - ref)) <= 5e-3 * np.max(np.abs(ref)) + 1e-3
 
 
+def check_qkv_composition(lib):
+    # closed form: x = 1, r = 0, gamma = 1, eps = 0 gives h = 1, sum of squares K,
+    # inv = 1 and xn = 1, so y_z[n] = s_n * (sum of row n's codes), exact in fp32
+    g = np.random.default_rng(71)
+    M, K = 2, 640
+    ns = (48, 16, 24)
+    vals = [g.integers(-2, 2, (n, K)).astype(np.int8) for n in ns]
+    scs = [synth.f16_bits(g.uniform(0.01, 0.05, n)) for n in ns]
+    x = synth.f16_bits(np.ones((M, K)))
+    r = synth.f16_bits(np.zeros((M, K)))
+    gm = synth.f16_bits(np.ones(K))
+    wq = [oracle.pack_int2(v, lib) for v in vals]
+    yq, yk, yv, res = oracle.int2_rmsnorm_qkv(x, r, gm, 0.0, wq[0], scs[0], wq[1], scs[1], wq[2], scs[2],
+                                              lib=lib)
+    assert np.array_equal(res, x)
+    for y, v, s in zip((yq, yk, yv), vals, scs):
+        exact = s.view(np.float16).astype(np.float64) * v.astype(np.int64).sum(axis=1)
+        assert np.array_equal(y, np.broadcast_to(exact.astype(np.float32), y.shape))
+    # random inputs: each output within a loose bound of the fp64 composition
+    d = synth.qkv_inputs(2, 40, 24, 24, 1536, salt=3)
+    outs = oracle.int2_rmsnorm_qkv(d["x"], d["residual"], d["gamma"], d["eps"], d["wq_q"], d["s_q"],
+                                   d["wq_k"], d["s_k"], d["wq_v"], d["s_v"], lib=lib)
+    for m in range(2):
+        xd = d["x"][m].view(np.float16).astype(np.float64)
+        rd = d["residual"][m].view(np.float16).astype(np.float64)
+        hd = (xd + rd).astype(np.float16).astype(np.float64)
+        assert np.array_equal(outs[3][m], (xd + rd).astype(np.float16).view(np.uint16))
+        xn = hd / math.sqrt(np.mean(hd * hd) + 1e-6) * d["gamma"].view(np.float16).astype(np.float64)
+        xn16 = xn.astype(np.float16).astype(np.float64)
+        for z, y in zip("qkv", outs[:3]):
+            w = oracle.unpack_int2(d["wq_" + z], 1536, lib).astype(np.float64)
+            yd = (w @ xn16) * d["s_" + z].view(np.float16).astype(np.float64)
+            assert np.max(np.abs(y[m] - yd)) <= 2e-3 * np.max(np.abs(yd)) + 1e-3
+
+
 # --------------------------------------------------------------- argmax ----
 
 def check_argmax_ties(lib):
@@ -442,5 +477,5 @@ ALL_CHECKS = [
     check_int2_vs_fp64, check_int4_vs_fp64, check_mxfp4_vs_fp64, check_integer_x_exact,
     check_single_segment_sequential, check_golden_order, check_threads_identical,
     check_exp_accuracy, check_gelu_accuracy, check_rmsnorm_vs_fp64, check_fused_composition,
-    check_argmax_ties,
+    check_qkv_composition, check_argmax_ties,
 ]
