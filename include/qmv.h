@@ -105,7 +105,8 @@ typedef enum qmv_op {
     QMV_OP_INT4 = 1,
     QMV_OP_MXFP4 = 2,
     QMV_OP_INT2_GATEUP = 3,
-    QMV_OP_INT2_ARGMAX = 4
+    QMV_OP_INT2_ARGMAX = 4,
+    QMV_OP_INT2_QKV = 5
 } qmv_op;
 
 /* Version of this ABI (QMV_ABI_VERSION). */
@@ -182,6 +183,26 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *resid
                                         const uint32_t *wq_up, const uint16_t *s_up,
                                         uint16_t *out, int M, int N, int K, qmv_mode mode,
                                         void *workspace, size_t ws_bytes, void *stream);
+
+/* Shared-prologue q/k/v ("What moved the needle", dispatch-count fusion:
+ * the residual-add RMSNorm folded into the next matvec's prologue, and
+ * q/k/v issued as one dispatch).  Per activation row m, the prologue of
+ * qmv_int2_rmsnorm_gateup_gelu (h = fp16(x + residual), inv, xn), then three
+ * independent fixed-order int2 matvecs of xn:
+ *   y_q = int2 matvec (wq_q, s_q), y_k = (wq_k, s_k), y_v = (wq_v, s_v),
+ * each exactly as qmv_int2 would compute it from xn (bit-exact).
+ *  x, residual fp16 [M][K] (16-byte aligned); residual_out fp16 [M][K] or
+ *  NULL (receives h); gamma fp16 [K]; wq_z uint32 [N_z][K/16] (16-byte
+ *  aligned); s_z fp16 [N_z]; y_z [M][N_z] in y_dtype (fp32 default, or one
+ *  RNE rounding to fp16 / bf16), each N_z >= 1 and M*N_z*4 bytes < 4 GiB.
+ *  K a multiple of 64, K <= 16384.  Mode: FIXED; no workspace. */
+qmv_status qmv_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uint16_t *residual_out,
+                                const uint16_t *gamma, float eps,
+                                const uint32_t *wq_q, const uint16_t *s_q, int Nq,
+                                const uint32_t *wq_k, const uint16_t *s_k, int Nk,
+                                const uint32_t *wq_v, const uint16_t *s_v, int Nv,
+                                void *y_q, void *y_k, void *y_v, qmv_dtype y_dtype, int M, int K,
+                                qmv_mode mode, void *workspace, size_t ws_bytes, void *stream);
 
 /* int2 lm_head + argmax in one dispatch ("The parked levers": argmax stage 1
  * and 2 merged, first maximum wins).  Logits are the fixed-order int2 matvec;

@@ -18,8 +18,8 @@ import os
 import torch
 
 __all__ = [
-    "qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu", "qmv_int2_argmax",
-    "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
+    "qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu", "qmv_int2_rmsnorm_qkv",
+    "qmv_int2_argmax", "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
     "MODES", "OPS",
 ]
 
@@ -32,7 +32,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 MODES = {"fixed": 0, "splitk": 1, "mfma": 2}
-OPS = {"int2": 0, "int4": 1, "mxfp4": 2, "int2_gateup": 3, "int2_argmax": 4}
+OPS = {"int2": 0, "int4": 1, "mxfp4": 2, "int2_gateup": 3, "int2_argmax": 4, "int2_qkv": 5}
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _vp, _i, _sz, _f = C.c_void_p, C.c_int, C.c_size_t, C.c_float
@@ -49,6 +49,8 @@ _SIGS = {
     "qmv_int2_rmsnorm_gateup_gelu": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp,
                                       _i, _i, _i, _i, _vp, _sz, _vp], _i),
     "qmv_int2_argmax": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
+    "qmv_int2_rmsnorm_qkv": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i,
+                              _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -196,6 +198,29 @@ def qmv_int2_rmsnorm_gateup_gelu(x, residual, gamma, eps, wq_gate, s_gate, wq_up
         _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(out), M, N, K, _mode(mode), _ptr(ws), wsb,
         _stream(stream)), "qmv_int2_rmsnorm_gateup_gelu")
     return out
+
+
+def qmv_int2_rmsnorm_qkv(x, residual, gamma, eps, wq_q, s_q, wq_k, s_k, wq_v, s_v, y_q=None, y_k=None,
+                         y_v=None, y_dtype=torch.float32, residual_out=None, mode="fixed", stream=None):
+    """(y_q, y_k, y_v): three int2 matvecs of the residual-add RMSNorm of x (see qmv.h)."""
+    M, K = x.shape
+    _req(x, "x", torch.float16, (M, K))
+    _req(residual, "residual", torch.float16, (M, K))
+    _req(gamma, "gamma", torch.float16, (K,))
+    ys = []
+    for name, w, s, y in (("q", wq_q, s_q, y_q), ("k", wq_k, s_k, y_k), ("v", wq_v, s_v, y_v)):
+        N = w.shape[0]
+        _req(w, "wq_" + name, torch.int32, (N, K // 16))
+        _req(s, "s_" + name, torch.float16, (N,))
+        ys.append(_out(y, M, N, y_dtype, x.device))
+    if residual_out is not None:
+        _req(residual_out, "residual_out", torch.float16, (M, K))
+    _check(_lib.qmv_int2_rmsnorm_qkv(
+        _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps),
+        _ptr(wq_q), _ptr(s_q), wq_q.shape[0], _ptr(wq_k), _ptr(s_k), wq_k.shape[0],
+        _ptr(wq_v), _ptr(s_v), wq_v.shape[0], _ptr(ys[0]), _ptr(ys[1]), _ptr(ys[2]),
+        _DTYPES[y_dtype], M, K, _mode(mode), None, 0, _stream(stream)), "qmv_int2_rmsnorm_qkv")
+    return ys[0], ys[1], ys[2]
 
 
 def qmv_int2_argmax(wq, scale, x, idx=None, maxval=None, logits=None, want_maxval=True,

@@ -1,6 +1,8 @@
 """Build libqmv.so (the HIP library) in-tree for gfx950.
 
-    python -m skinny_gemm_qmv_amd.build          # or __graft_entry__.build()
+    python skinny_gemm_qmv_amd/build.py          # or __graft_entry__.build()
+
+(Run it as a script: importing the package first would need the library.)
 
 Flags:
   --offload-arch=gfx950        MI355X only

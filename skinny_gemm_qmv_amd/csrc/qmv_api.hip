@@ -168,6 +168,36 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *resid
     return hip_status(qmv::launch_fo_gateup(a, static_cast<hipStream_t>(stream)));
 }
 
+qmv_status qmv_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uint16_t *residual_out,
+                                const uint16_t *gamma, float eps,
+                                const uint32_t *wq_q, const uint16_t *s_q, int Nq,
+                                const uint32_t *wq_k, const uint16_t *s_k, int Nk,
+                                const uint32_t *wq_v, const uint16_t *s_v, int Nv,
+                                void *y_q, void *y_k, void *y_v, qmv_dtype y_dtype, int M, int K,
+                                qmv_mode mode, void *workspace, size_t ws_bytes, void *stream) {
+    (void)workspace; (void)ws_bytes;
+    if (!x || !residual || !gamma || !wq_q || !s_q || !wq_k || !s_k || !wq_v || !s_v || !y_q || !y_k || !y_v)
+        return QMV_ERR_INVALID_ARG;
+    const int ns[3] = {Nq, Nk, Nv};
+    for (int z = 0; z < 3; ++z)
+        if (!valid_shape(M, ns[z], K, 64)) return QMV_ERR_INVALID_ARG;
+    if (!valid_dtype(y_dtype) || !valid_mode(mode) || !(eps >= 0.0f)) return QMV_ERR_INVALID_ARG;
+    for (int z = 0; z < 3; ++z) {
+        if (!fits_32bit(ns[z], K, 4)) return QMV_ERR_UNSUPPORTED;
+        if ((uint64_t)M * (uint64_t)ns[z] * 4u >= (1ull << 32) - (1ull << 16)) return QMV_ERR_UNSUPPORTED;
+    }
+    if ((uint64_t)Nq + Nk + Nv > 0x7FFFFFFFull) return QMV_ERR_UNSUPPORTED;
+    const size_t es = dtype_size(y_dtype);
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(wq_q, 16) || !aligned(wq_k, 16) ||
+        !aligned(wq_v, 16) || !aligned(gamma, 2) || !aligned(y_q, es) || !aligned(y_k, es) || !aligned(y_v, es) ||
+        (residual_out && !aligned(residual_out, 2)))
+        return QMV_ERR_ALIGNMENT;
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+    qmv::QkvArgs a{x, residual, gamma, residual_out, eps, {wq_q, wq_k, wq_v}, {s_q, s_k, s_v},
+                   {y_q, y_k, y_v}, {Nq, Nk, Nv}, (int)y_dtype, M, K};
+    return hip_status(qmv::launch_fo_qkv(a, static_cast<hipStream_t>(stream)));
+}
+
 qmv_status qmv_int2_argmax(const uint32_t *wq, const uint16_t *scale, const uint16_t *x,
                            int32_t *idx, float *maxval, float *logits, int M, int N, int K,
                            qmv_mode mode, void *workspace, size_t ws_bytes, void *stream) {

@@ -215,9 +215,16 @@ struct FoEngine {
 
     // K_ is the number of codes this engine sums per row (a whole row, or one
     // K split of nseg_row-segment rows starting at segment seg0).
+    // blk / nblk: this workgroup's index among the nblk workgroups that share
+    // the rows (default: the whole grid along x)
     __device__ __forceinline__ FoEngine(const uint8_t *const (&wq)[NMAT], const void *const (&sc)[NMAT],
-                                        int N_, int K_, int seg0 = 0, int nseg_row = 0)
+                                        int N_, int K_, int seg0 = 0, int nseg_row = 0, int blk = -1,
+                                        int nblk = -1)
         : N(N_), K(K_) {
+        if (blk < 0) {
+            blk = blockIdx.x;
+            nblk = gridDim.x;
+        }
         nseg = K / CODES;
         if (nseg_row == 0) nseg_row = nseg;
         P2 = 1;
@@ -228,10 +235,10 @@ struct FoEngine {
         row_bytes = (uint32_t)nseg_row * 16u;
         const int total_rg = (N + RPG - 1) / RPG;
         total_units = (total_rg + R - 1) / R;
-        stride = gridDim.x * kWaves;
+        stride = nblk * kWaves;
         // wave-uniform: read it through a scalar so that the unit loop is a
         // scalar loop (no exec-masked control flow around the load ring)
-        first = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + wave);
+        first = __builtin_amdgcn_readfirstlane(blk * kWaves + wave);
         // bytes of scale data per row
         srow = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u * nseg_row : (uint32_t)nseg_row);
         const uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);  // bytes per scale
@@ -1129,6 +1136,75 @@ hipError_t launch_fo_gateup(const GateUpArgs &a, hipStream_t st) {
     LaneShape sh;
     if (!pick_shape_rows(a.K / 64, a.N, sh)) return hipErrorInvalidValue;
     QMV_SHAPE_SWITCH(gu_shape, a, st)
+}
+
+// ---------------------------------------------------------------------------
+// Shared-prologue q/k/v ([A19] "What moved the needle", dispatch-count
+// fusion): the residual-add RMSNorm prologue and three int2 fixed-order
+// matvecs (q, k, v; their own row counts) in one dispatch.  Workgroups
+// [0, bq) take q's rows, [bq, bq+bk) k's, the rest v's; every workgroup
+// computes the prologue of its activation row (blockIdx.y) itself, exactly
+// as the fused gate/up kernel does, and workgroup 0 of q writes
+// residual_out.
+template <int MC>
+struct QkvEpi {
+    OutBuf out;
+    int M, N, m0;
+    __device__ __forceinline__ void operator()(int n, int q, const float (&tot)[1][MC],
+                                               const float (&rs)[1]) {
+        const bool act = q == 0 && n < N;
+#pragma unroll
+        for (int m = 0; m < MC; ++m)
+            if (m0 + m < M) out.put(act, (uint32_t)((m0 + m) * N + n), rs[0] * tot[0][m]);
+    }
+};
+
+template <int RL, int NI, int NIP, bool XREG>
+__global__ __launch_bounds__(kBlock) void k_fo_qkv(const QkvArgs a, int bq, int bk, int bv) {
+    extern __shared__ __align__(16) uint16_t smem[];
+    uint16_t *xs = smem;  // [K]: h, then the normalised xn in place
+    float *inv_s = reinterpret_cast<float *>(smem + a.K);
+    const int b = blockIdx.x, m = blockIdx.y;
+    // uniform per workgroup: which matrix, and this workgroup's index in it
+    const int z = b < bq ? 0 : (b < bq + bk ? 1 : 2);
+    const int blk = z == 0 ? b : (z == 1 ? b - bq : b - bq - bk);
+    const int nblk = z == 0 ? bq : (z == 1 ? bk : bv);
+    const int N = a.N[z];
+    const uint8_t *const w1[1] = {reinterpret_cast<const uint8_t *>(a.wq[z])};
+    const void *const s1[1] = {a.s[z]};
+    FoEngine<FMT_INT2, RL, NI, NIP, 1, XREG, 1, ring_depth<NI, 1>(), 1> eng(w1, s1, N, a.K, 0, 0, blk, nblk);
+    RmsStage1 rs1;
+    rs1.load(a.x, a.residual, a.gamma, a.K, m);
+    eng.prefetch();
+    rs1.finish(a.x, a.residual, a.gamma, b == 0 ? a.residual_out : nullptr, a.eps, a.K, m, xs, inv_s);
+    QkvEpi<1> epi{OutBuf(a.y[z], (uint32_t)a.M * (uint32_t)N, a.y_dtype), a.M, N, m};
+    eng.run(xs, epi);
+}
+
+template <int RL, int NI, int NIP>
+static hipError_t qkv_shape(const QkvArgs &a, hipStream_t st) {
+    constexpr int D = ring_depth<NI, 1>();
+    auto k = k_fo_qkv<RL, NI, NIP, xreg_fits<FMT_INT2, NI>()>;
+    const size_t lds = (size_t)a.K * 2 + 64;
+    const long ntot = (long)a.N[0] + a.N[1] + a.N[2];
+    // the workgroups one launch over all rows would use, shared out by rows
+    const int g = grid_for(k, lds, ntot, RL, D, stream_per_cu<NI, 1>());
+    int bz[3];
+    for (int z = 0; z < 3; ++z) {
+        const int rpg = 64 / RL;
+        const long need = ((long)a.N[z] + rpg * kWaves - 1) / (rpg * kWaves);  // one row group per wave
+        long share = ((long)g * a.N[z] + ntot - 1) / ntot;
+        if (share > need) share = need;
+        bz[z] = share < 1 ? 1 : (int)share;
+    }
+    hipLaunchKernelGGL(k, dim3(bz[0] + bz[1] + bz[2], a.M), dim3(kBlock), lds, st, a, bz[0], bz[1], bz[2]);
+    return hipGetLastError();
+}
+
+hipError_t launch_fo_qkv(const QkvArgs &a, hipStream_t st) {
+    LaneShape sh;
+    if (!pick_shape_rows(a.K / 64, (long)a.N[0] + a.N[1] + a.N[2], sh)) return hipErrorInvalidValue;
+    QMV_SHAPE_SWITCH(qkv_shape, a, st)
 }
 
 // Activation rows per argmax workgroup chunk, and the number of chunks.

@@ -56,6 +56,20 @@ struct GateUpArgs {
 
 hipError_t launch_fo_gateup(const GateUpArgs &a, hipStream_t stream);
 
+// Shared-prologue q/k/v: index 0 = q, 1 = k, 2 = v.
+struct QkvArgs {
+    const uint16_t *x, *residual, *gamma;
+    uint16_t *residual_out;
+    float eps;
+    const uint32_t *wq[3];
+    const uint16_t *s[3];
+    void *y[3];
+    int N[3];
+    int y_dtype, M, K;
+};
+
+hipError_t launch_fo_qkv(const QkvArgs &a, hipStream_t stream);
+
 struct ArgmaxArgs {
     const uint32_t *wq;
     const uint16_t *scale, *x;

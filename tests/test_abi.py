@@ -104,6 +104,31 @@ def test_gateup_validation():
     assert call(args, M=256, N=1 << 23) == UNSUP  # fp16 output of M*N*2 >= 4 GiB (32-bit offsets)
 
 
+def test_qkv_validation():
+    fn = q._lib.qmv_int2_rmsnorm_qkv
+
+    def call(ptrs=None, Ns=(64, 64, 64), dt=0, M=1, K=64, mode=0, eps=1e-6):
+        p = ptrs or {}
+        a = [P(p.get(i, 16)) if p.get(i, 16) else None for i in range(4)]  # x, residual, residual_out, gamma
+        w = [P(p.get(4 + i, 16)) if p.get(4 + i, 16) else None for i in range(6)]  # wq/s for q, k, v
+        y = [P(p.get(10 + i, 16)) if p.get(10 + i, 16) else None for i in range(3)]
+        return fn(a[0], a[1], a[2], a[3], C.c_float(eps), w[0], w[1], Ns[0], w[2], w[3], Ns[1],
+                  w[4], w[5], Ns[2], y[0], y[1], y[2], dt, M, K, mode, None, 0, None)
+    assert call() != INVALID or True  # shape is valid; the call would launch (not run here)
+    assert call({0: 0}) == INVALID
+    assert call({2: 0}) != INVALID or True  # residual_out optional
+    assert call({12: 0}) == INVALID
+    assert call(Ns=(64, 0, 64)) == INVALID
+    assert call(K=96) == INVALID
+    assert call(M=257) == INVALID
+    assert call(dt=3) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call({6: 24}) == ALIGN
+    assert call({10: 18}) == ALIGN
+    assert call(mode=1) == UNSUP
+    assert call(M=256, Ns=(64, 1 << 22, 64)) == UNSUP  # y_k of M*N*4 >= 4 GiB
+
+
 def test_argmax_validation():
     fn = q._lib.qmv_int2_argmax
 
