@@ -183,6 +183,24 @@ def sweep_cases():
             x, r, gm, 1e-6, wg[i % cp], sg[i % cp], wu[i % cp], su[i % cp], out=out,
             residual_out=ro))), nb, 2 * 2 * 8192 * 1536, "hbm"
 
+    def qkv_f1():
+        # q/k/v shapes of a K=1536 decoder layer: 8 query heads and 2 key/value
+        # heads of 256 (synthetic int2 weights, the fused workload's recipe)
+        Nq, Nk, Nv, K = 2048, 512, 512, 1536
+        d = synth.qkv_inputs(1, Nq, Nk, Nv, K)
+        wb = (Nq + Nk + Nv) * (K // 4 + 2)
+        cp = -(-COLD_BYTES // wb)
+        ws = {z: rotating(dev(d["wq_" + z], "u32"), cp) for z in "qkv"}
+        ss = {z: rotating(dev(d["s_" + z], "f16"), cp) for z in "qkv"}
+        x, r, gm = dev(d["x"], "f16"), dev(d["residual"], "f16"), dev(d["gamma"], "f16")
+        ys = [torch.empty((1, n), device="cuda") for n in (Nq, Nk, Nv)]
+        ro = torch.empty((1, K), dtype=torch.float16, device="cuda")
+        nb = wb + 3 * K * 2 + K * 2 + (Nq + Nk + Nv) * 4
+        return (lambda i: (lambda: q.qmv_int2_rmsnorm_qkv(
+            x, r, gm, 1e-6, ws["q"][i % cp], ss["q"][i % cp], ws["k"][i % cp], ss["k"][i % cp],
+            ws["v"][i % cp], ss["v"][i % cp], y_q=ys[0], y_k=ys[1], y_v=ys[2], residual_out=ro))), \
+            nb, 2 * (Nq + Nk + Nv) * K, "hbm"
+
     def argmax_c4(M):
         def b():
             d = synth.argmax_inputs(M, 262144, 1536, workload=4)
@@ -224,6 +242,7 @@ def sweep_cases():
         ("int4 N=16384 K=4096 M=8", int4_m(8)),
         ("int4 N=16384 K=4096 M=16", int4_m(16)),
         ("fused rmsnorm+int2 gate/up+gelu N=2x8192 K=1536 M=1", fused_c3),
+        ("fused rmsnorm+int2 q/k/v N=2048+512+512 K=1536 M=1", qkv_f1),
         ("int2 lm_head+argmax N=262144 K=1536 M=1", argmax_c4(1)),
         ("int2 lm_head+argmax N=262144 K=1536 M=4", argmax_c4(4)),
         ("mxfp4 N=21504 K=5376 M=1", mxfp4_m(1)),
