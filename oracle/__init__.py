@@ -67,6 +67,7 @@ def _bind(lib):
         "orc_int2_rmsnorm_gateup_gelu": ([vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp,
                                           i64, i64, i64, i32], None),
         "orc_int2_argmax": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32], None),
+        "orc_qmm_mxfp4_gather": ([vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32], None),
         "orc_int2_rmsnorm_qkv": ([vp, vp, vp, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64,
                                   vp, vp, vp, i64, i64, i32], None),
         "orc_ref64_int2": ([vp, vp, vp, vp, vp, i64, i64, i64], None),
@@ -127,6 +128,20 @@ def qmm_mxfp4(wq, e8m0, x, threads=None, lib=None):
     assert wq.shape[1] * 2 == K and e8m0.shape == (N, K // 32) and K % 32 == 0
     y = np.empty((M, N), np.float32)
     lib.orc_qmm_mxfp4(_p(wq), _p(e8m0), _p(x), _p(y), M, N, K, threads or default_threads())
+    return y
+
+
+def qmm_mxfp4_gather(wq, e8m0, x, idx, threads=None, lib=None):
+    """Expert-gather FO MXFP4 matvec. wq uint8 [E][N][K/2], e8m0 uint8 [E][N][K/32],
+    x bf16 bits [M][K], idx int32 [M][topk] in [0, E).  Returns y fp32 [M][topk][N]."""
+    lib = lib or load()
+    wq, e8m0, x, idx = _c(wq, np.uint8), _c(e8m0, np.uint8), _c(x, np.uint16), _c(idx, np.int32)
+    E, N, M, K, topk = wq.shape[0], wq.shape[1], x.shape[0], x.shape[1], idx.shape[1]
+    assert wq.shape[2] * 2 == K and e8m0.shape == (E, N, K // 32) and idx.shape[0] == M
+    assert np.all((idx >= 0) & (idx < E))
+    y = np.empty((M, topk, N), np.float32)
+    lib.orc_qmm_mxfp4_gather(_p(wq), _p(e8m0), _p(x), _p(idx), _p(y), E, topk, M, N, K,
+                             threads or default_threads())
     return y
 
 

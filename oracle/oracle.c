@@ -23,7 +23,9 @@
  *         Section "The parked levers": argmax with the first-max tie-break.
  *  [PB]   "raw-Metal loop playbook", prefill route table: for M = 8/16 keep
  *         every output scalar's K-dot in the M = 1 accumulation order while
- *         the weights are shared across the M columns.
+ *         the weights are shared across the M columns.  Next-target ranking
+ *         table: an expert-gather matvec that reads the selected experts'
+ *         weights in place (gpt-oss MoE).
  *  [GEM]  "Gemma 4 Optimization with Agentic Kernel Engineering", sections
  *         "A new chip, the same model" and "How much of the chip we use now":
  *         MXFP4 weights on MI355X.  The MXFP4 element and scale encodings are
@@ -450,6 +452,25 @@ ORC_API void orc_qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_
     mv_ctx c = {wq, e8m0, xf, y, M, N, K};
     parallel_rows(mxfp4_rows, &c, N, nthreads);
     free(xf);
+}
+
+/* Expert-gather MXFP4 matvec ([PB], next-target ranking table, the gpt-oss MoE
+ * row: close the gather_qmm frontier with a zero-materialisation expert-gather
+ * matvec).  E experts' weights wq [E][N][K/2], e8m0 [E][N][K/32]; for activation
+ * row m and slot j the expert e = idx[m][j] selects its weights in place (no
+ * gathered copy) and y[m][j][N] = the FO MXFP4 matvec of expert e with x[m].
+ * Every idx entry must lie in [0, E). */
+ORC_API void orc_qmm_mxfp4_gather(const uint8_t *wq, const uint8_t *e8m0, const uint16_t *x,
+                                  const int32_t *idx, float *y, int64_t E, int64_t topk, int64_t M,
+                                  int64_t N, int64_t K, int nthreads)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < topk; ++j) {
+            const int64_t e = idx[m * topk + j];
+            if (e < 0 || e >= E) abort();
+            orc_qmm_mxfp4(wq + e * N * (K / 2), e8m0 + e * N * (K / 32), x + m * K,
+                          y + (m * topk + j) * N, 1, N, K, nthreads);
+        }
 }
 
 /* ------------------------------------------------------------------------ */

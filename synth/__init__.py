@@ -20,6 +20,9 @@ Workloads (the shapes the benchmark and the parity tests use):
   3  fused RMSNorm -> int2 gate/up -> GELU*up   M=1, N=8192 (x2), K=1536
   4  int2 lm_head + argmax   M in {1,4}, N=262144, K=1536
   5  MXFP4 GEMM         M in {1,16,64,256}, N=21504, K=5376, x bf16
+  6  fused RMSNorm -> int2 q/k/v   M=1, N=2048+512+512, K=1536
+  7  MXFP4 expert gather  M=1, E=32 experts, topk=4, N=5760, K=2880 (a gpt-oss-sized
+                          MoE up/gate projection; ids drawn uniformly without repeats)
 """
 import numpy as np
 
@@ -109,6 +112,18 @@ def qkv_inputs(M, Nq, Nk, Nv, K, workload=6, salt=0):
 
 def argmax_inputs(M, N, K, workload=4, salt=0):
     return int2_inputs(M, N, K, workload=workload, salt=salt)
+
+
+def expert_inputs(M, E, topk, N, K, workload=7, salt=0, exp_range=(-8, 2)):
+    """E experts of MXFP4 weights (the MXFP4 recipe: E2M1 nibbles uniform, E8M0 = 127 +
+    U{-8..2}) [E][N][K/2] + [E][N][K/32], bf16 x [M][K] ~N(0,1), and for each row topk
+    distinct expert ids drawn uniformly (int32 [M][topk])."""
+    g = rng(workload, M, salt)
+    wq = raw_bytes(g, (E, N, K // 2))
+    e8m0 = (127 + g.integers(exp_range[0], exp_range[1] + 1, size=(E, N, K // 32))).astype(np.uint8)
+    x = bf16_bits(g.standard_normal((M, K)))
+    idx = np.stack([g.permutation(E)[:topk] for _ in range(M)]).astype(np.int32)
+    return dict(wq=wq, e8m0=e8m0, x=x, idx=idx)
 
 
 def mxfp4_inputs(M, N, K, workload=5, salt=0, exp_range=(-8, 2)):

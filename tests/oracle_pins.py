@@ -438,6 +438,36 @@ def check_qkv_composition(lib):
             assert np.max(np.abs(y[m] - yd)) <= 2e-3 * np.max(np.abs(yd)) + 1e-3
 
 
+def check_expert_gather(lib):
+    # closed form: expert e has every element 1.0 (E2M1 code 2) and every block
+    # scale 2^e; with integer x the output is exactly 2^idx * sum(x), so each
+    # output names the expert it was computed from
+    g = np.random.default_rng(81)
+    E, M, topk, N, K = 6, 3, 4, 5, 96
+    wq = np.full((E, N, K // 2), 0x22, np.uint8)
+    e8 = np.broadcast_to((127 + np.arange(E, dtype=np.uint8))[:, None, None], (E, N, K // 32)).copy()
+    xi = g.integers(-4, 5, (M, K))
+    x = synth.bf16_bits(xi.astype(np.float64))
+    idx = np.array([[5, 0, 3, 3], [1, 2, 4, 0], [0, 0, 0, 0]], np.int32)  # duplicates allowed
+    y = oracle.qmm_mxfp4_gather(wq, e8, x, idx, lib=lib)
+    want = np.ldexp(1.0, idx)[:, :, None] * xi.sum(axis=1)[:, None, None]
+    assert np.array_equal(y, np.broadcast_to(want, y.shape).astype(np.float32))
+    # random experts: within the fixed-order bound of brute-force fp64 on the selected expert
+    d = synth.expert_inputs(2, 8, 3, 24, 256, salt=1)
+    y = oracle.qmm_mxfp4_gather(d["wq"], d["e8m0"], d["x"], d["idx"], lib=lib)
+    table = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
+    xd = d["x"].astype(np.uint32).astype(np.uint64) << np.uint64(16)
+    xd = xd.astype(np.uint32).view(np.float32).astype(np.float64)
+    for m in range(2):
+        for j in range(3):
+            e = int(d["idx"][m, j])
+            nib = np.stack([d["wq"][e] & 15, d["wq"][e] >> 4], axis=-1).reshape(24, 256)
+            w = table[nib] * np.repeat(np.ldexp(1.0, d["e8m0"][e].astype(int) - 127), 32, axis=1)
+            exact = w @ xd[m]
+            mag = np.abs(w) @ np.abs(xd[m])
+            assert np.all(np.abs(y[m, j] - exact) <= gamma(32 + 3 + 1) * mag)
+
+
 # --------------------------------------------------------------- argmax ----
 
 def check_argmax_ties(lib):
@@ -477,5 +507,5 @@ ALL_CHECKS = [
     check_int2_vs_fp64, check_int4_vs_fp64, check_mxfp4_vs_fp64, check_integer_x_exact,
     check_single_segment_sequential, check_golden_order, check_threads_identical,
     check_exp_accuracy, check_gelu_accuracy, check_rmsnorm_vs_fp64, check_fused_composition,
-    check_qkv_composition, check_argmax_ties,
+    check_qkv_composition, check_expert_gather, check_argmax_ties,
 ]
