@@ -144,6 +144,7 @@ def int4_case(M, cold=True):
 
 def sweep_cases():
     """(label, builder) for the other workloads; builder() -> (make_call, bytes, flops, bound)."""
+    import numpy as np
     import torch
     import skinny_gemm_qmv_amd as q
     import synth
@@ -201,6 +202,26 @@ def sweep_cases():
             ws["v"][i % cp], ss["v"][i % cp], y_q=ys[0], y_k=ys[1], y_v=ys[2], residual_out=ro))), \
             nb, 2 * (Nq + Nk + Nv) * K, "hbm"
 
+    def gather_f2(M):
+        # a gpt-oss-sized MoE projection: 32 MXFP4 experts of N=5760, K=2880,
+        # each activation row routed to 4 of them; every step picks other
+        # experts (a fresh id draw) from enough copies of the expert array that
+        # the weights are read cold
+        def b():
+            E, topk, N, K = 32, 4, 5760, 2880
+            d = synth.expert_inputs(M, E, topk, N, K)
+            eb = N * K // 2 + N * (K // 32)
+            cp = -(-COLD_BYTES // (E * eb))
+            wq, e = rotating(dev(d["wq"], "u8"), cp), rotating(dev(d["e8m0"], "u8"), cp)
+            x = dev(d["x"], "bf16")
+            g = synth.rng(7, M, 1)
+            ids = [torch.from_numpy(np.stack([g.permutation(E)[:topk] for _ in range(M)]).astype(np.int32)).cuda()
+                   for _ in range(8)]
+            y = torch.empty((M, topk, N), device="cuda")
+            return (lambda i: (lambda: q.qmm_mxfp4_gather(wq[i % cp], e[i % cp], x, ids[i % 8], y=y))), \
+                M * topk * eb + M * K * 2 + M * topk * 4 + M * topk * N * 4, 2 * M * topk * N * K, "hbm"
+        return b
+
     def argmax_c4(M):
         def b():
             d = synth.argmax_inputs(M, 262144, 1536, workload=4)
@@ -243,6 +264,7 @@ def sweep_cases():
         ("int4 N=16384 K=4096 M=16", int4_m(16)),
         ("fused rmsnorm+int2 gate/up+gelu N=2x8192 K=1536 M=1", fused_c3),
         ("fused rmsnorm+int2 q/k/v N=2048+512+512 K=1536 M=1", qkv_f1),
+        ("mxfp4 expert gather E=32 top-4 N=5760 K=2880 M=1", gather_f2(1)),
         ("int2 lm_head+argmax N=262144 K=1536 M=1", argmax_c4(1)),
         ("int2 lm_head+argmax N=262144 K=1536 M=4", argmax_c4(4)),
         ("mxfp4 N=21504 K=5376 M=1", mxfp4_m(1)),

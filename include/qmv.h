@@ -106,7 +106,8 @@ typedef enum qmv_op {
     QMV_OP_MXFP4 = 2,
     QMV_OP_INT2_GATEUP = 3,
     QMV_OP_INT2_ARGMAX = 4,
-    QMV_OP_INT2_QKV = 5
+    QMV_OP_INT2_QKV = 5,
+    QMV_OP_MXFP4_GATHER = 6
 } qmv_op;
 
 /* Version of this ABI (QMV_ABI_VERSION). */
@@ -214,6 +215,25 @@ qmv_status qmv_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uin
 qmv_status qmv_int2_argmax(const uint32_t *wq, const uint16_t *scale, const uint16_t *x,
                            int32_t *idx, float *maxval, float *logits, int M, int N, int K,
                            qmv_mode mode, void *workspace, size_t ws_bytes, void *stream);
+
+/* Expert-gather MXFP4 matvec ("raw-Metal loop playbook", next-target ranking
+ * table: the gpt-oss MoE row, a zero-materialisation expert-gather matvec).
+ * The weights of E experts sit side by side; activation row m routes to the
+ * topk experts idx[m][0 .. topk); each is read in place (no gathered copy):
+ *   y[m][j][n] = qmm_mxfp4 fixed-order output (m, n) computed with expert
+ *                e = idx[m][j]'s rows wq[e], e8m0[e] and activation row x[m]
+ * (bit-exact with qmm_mxfp4 FIXED on the slices wq[e], e8m0[e], x[m]).
+ *  wq uint8 [E][N][K/2] (16-byte aligned); e8m0 uint8 [E][N][K/32];
+ *  x bf16 [M][K] (16-byte aligned); idx int32 [M][topk] on the device;
+ *  y [M][topk][N] in y_dtype (fp32, or one RNE rounding to fp16 / bf16).
+ *  E >= 1, topk >= 1, M*topk <= 65535, one expert's N*K/2 bytes and
+ *  M*topk*N*4 bytes < 4 GiB; K a multiple of 32, K <= 16384.
+ *  An id outside [0, E) cannot be seen at the call (idx stays on the device):
+ *  that plane y[m][j][*] is set to NaN and no memory outside wq / e8m0 is
+ *  read.  Duplicate ids in a row are allowed.  Mode: FIXED; no workspace. */
+qmv_status qmm_mxfp4_gather(const uint8_t *wq, const uint8_t *e8m0, int E, const uint16_t *x,
+                            const int32_t *idx, int topk, void *y, qmv_dtype y_dtype, int M, int N, int K,
+                            qmv_mode mode, void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

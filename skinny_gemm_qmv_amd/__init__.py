@@ -10,6 +10,7 @@ Tensor conventions (all on the GPU, contiguous, row-major):
   int2 weights  torch.int32 [N, K/16]  (bit patterns of uint32 words)
   int4 weights  torch.int32 [N, K/8]
   MXFP4 weights torch.uint8 [N, K/2];  E8M0 scales torch.uint8 [N, K/32]
+  MXFP4 experts torch.uint8 [E, N, K/2] and [E, N, K/32]; expert ids torch.int32
   fp16 tensors  torch.float16;  bf16 tensors torch.bfloat16
 """
 import ctypes as C
@@ -19,7 +20,7 @@ import torch
 
 __all__ = [
     "qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu", "qmv_int2_rmsnorm_qkv",
-    "qmv_int2_argmax", "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
+    "qmv_int2_argmax", "qmm_mxfp4_gather", "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
     "MODES", "OPS",
 ]
 
@@ -32,7 +33,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 MODES = {"fixed": 0, "splitk": 1, "mfma": 2}
-OPS = {"int2": 0, "int4": 1, "mxfp4": 2, "int2_gateup": 3, "int2_argmax": 4, "int2_qkv": 5}
+OPS = {"int2": 0, "int4": 1, "mxfp4": 2, "int2_gateup": 3, "int2_argmax": 4, "int2_qkv": 5, "mxfp4_gather": 6}
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _vp, _i, _sz, _f = C.c_void_p, C.c_int, C.c_size_t, C.c_float
@@ -51,6 +52,7 @@ _SIGS = {
     "qmv_int2_argmax": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
     "qmv_int2_rmsnorm_qkv": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i,
                               _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
+    "qmm_mxfp4_gather": ([_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -221,6 +223,26 @@ def qmv_int2_rmsnorm_qkv(x, residual, gamma, eps, wq_q, s_q, wq_k, s_k, wq_v, s_
         _ptr(wq_v), _ptr(s_v), wq_v.shape[0], _ptr(ys[0]), _ptr(ys[1]), _ptr(ys[2]),
         _DTYPES[y_dtype], M, K, _mode(mode), None, 0, _stream(stream)), "qmv_int2_rmsnorm_qkv")
     return ys[0], ys[1], ys[2]
+
+
+def qmm_mxfp4_gather(wq, e8m0, x, idx, y=None, y_dtype=torch.float32, mode="fixed", stream=None):
+    """Expert-gather MXFP4 matvec (see qmv.h).  wq uint8 [E,N,K/2], e8m0 uint8 [E,N,K/32],
+    x bf16 [M,K], idx int32 [M,topk].  Returns y [M,topk,N]."""
+    M, K = x.shape
+    E, N = wq.shape[0], wq.shape[1]
+    topk = idx.shape[1] if idx.dim() == 2 else -1
+    _req(wq, "wq", torch.uint8, (E, N, K // 2))
+    _req(e8m0, "e8m0", torch.uint8, (E, N, K // 32))
+    _req(x, "x", torch.bfloat16, (M, K))
+    _req(idx, "idx", torch.int32, (M, topk))
+    if y is None:
+        y = torch.empty((M, topk, N), dtype=y_dtype, device=x.device)
+    else:
+        _req(y, "y", y_dtype, (M, topk, N))
+    _check(_lib.qmm_mxfp4_gather(_ptr(wq), _ptr(e8m0), E, _ptr(x), _ptr(idx), topk, _ptr(y),
+                                 _DTYPES[y_dtype], M, N, K, _mode(mode), None, 0, _stream(stream)),
+           "qmm_mxfp4_gather")
+    return y
 
 
 def qmv_int2_argmax(wq, scale, x, idx=None, maxval=None, logits=None, want_maxval=True,

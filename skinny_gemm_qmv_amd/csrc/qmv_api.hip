@@ -19,6 +19,9 @@ qmv_status hip_status(hipError_t e) {
     return QMV_ERR_HIP;
 }
 
+// Largest grid.y of a launch.
+constexpr long kMaxGridY = 65535;
+
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t dtype_size(qmv_dtype d) { return d == QMV_F32 ? 4 : 2; }
@@ -196,6 +199,24 @@ qmv_status qmv_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uin
     qmv::QkvArgs a{x, residual, gamma, residual_out, eps, {wq_q, wq_k, wq_v}, {s_q, s_k, s_v},
                    {y_q, y_k, y_v}, {Nq, Nk, Nv}, (int)y_dtype, M, K};
     return hip_status(qmv::launch_fo_qkv(a, static_cast<hipStream_t>(stream)));
+}
+
+qmv_status qmm_mxfp4_gather(const uint8_t *wq, const uint8_t *e8m0, int E, const uint16_t *x,
+                            const int32_t *idx, int topk, void *y, qmv_dtype y_dtype, int M, int N, int K,
+                            qmv_mode mode, void *workspace, size_t ws_bytes, void *stream) {
+    (void)workspace; (void)ws_bytes;
+    if (!wq || !e8m0 || !x || !idx || !y) return QMV_ERR_INVALID_ARG;
+    if (!valid_shape(M, N, K, 32) || E < 1 || topk < 1 || !valid_dtype(y_dtype) || !valid_mode(mode))
+        return QMV_ERR_INVALID_ARG;
+    // one expert is addressed with 32-bit offsets; planes go along grid.y
+    if (!fits_32bit(N, K, 2) || (long)M * topk > kMaxGridY) return QMV_ERR_UNSUPPORTED;
+    if ((uint64_t)M * (uint64_t)topk * (uint64_t)N * 4u >= (1ull << 32) - (1ull << 16))
+        return QMV_ERR_UNSUPPORTED;
+    if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(idx, 4) || !aligned(y, dtype_size(y_dtype)))
+        return QMV_ERR_ALIGNMENT;
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+    qmv::GatherArgs a{wq, e8m0, x, idx, y, (int)y_dtype, E, topk, M, N, K};
+    return hip_status(qmv::launch_fo_gather(a, static_cast<hipStream_t>(stream)));
 }
 
 qmv_status qmv_int2_argmax(const uint32_t *wq, const uint16_t *scale, const uint16_t *x,

@@ -1207,6 +1207,59 @@ hipError_t launch_fo_qkv(const QkvArgs &a, hipStream_t st) {
     QMV_SHAPE_SWITCH(qkv_shape, a, st)
 }
 
+// ---------------------------------------------------------------------------
+// Expert-gather MXFP4 matvec: output plane p = (m, j), m = p / topk, is the
+// fixed-order matvec of activation row m with expert e = idx[p], read in
+// place (no gathered copy of the weights).  grid.y = the M*topk planes; the
+// workgroups along x share the plane's rows like a plain M = 1 launch.  The
+// expert's weights and scales are addressed through buffer descriptors that
+// cover that expert only, so no load reaches another expert's rows.  An id
+// outside [0, E) reads nothing and sets the plane's outputs to NaN.
+template <int RL, int NI, int NIP, bool XREG>
+__global__ __launch_bounds__(kBlock) void k_fo_gather(const GatherArgs a) {
+    extern __shared__ __align__(16) uint16_t xs[];
+    const int p = blockIdx.y;
+    const int m = p / a.topk;
+    const int e = __builtin_amdgcn_readfirstlane(a.idx[p]);
+    const uint32_t total = (uint32_t)a.M * (uint32_t)a.topk * (uint32_t)a.N;
+    if (e < 0 || e >= a.E) {  // uniform over the workgroup
+        const OutBuf out(a.y, total, a.y_dtype);
+        for (int n = blockIdx.x * kBlock + threadIdx.x; n < a.N; n += gridDim.x * kBlock)
+            out.put(true, (uint32_t)p * a.N + n, __builtin_nanf(""));
+        return;
+    }
+    const uint8_t *const w1[1] = {a.wq + (size_t)e * a.N * (a.K / 2)};
+    const void *const s1[1] = {a.e8m0 + (size_t)e * a.N * (a.K / 32)};
+    FoEngine<FMT_MXFP4, RL, NI, NIP, 1, XREG, 1, ring_depth<NI, 1>(), 1> eng(w1, s1, a.N, a.K);
+    const uint16_t *xm = a.x + (size_t)m * a.K;
+    XStage<1> xst;
+    xst.load(xm, 1, a.K, a.K, 0);
+    eng.prefetch();
+    xst.store(xm, xs, 1, a.K, a.K, 0);
+    __syncthreads();
+    StoreEpi<FMT_MXFP4, 1> epi{OutBuf(a.y, total, a.y_dtype), false, a.M * a.topk, a.N, p};
+    eng.run(xs, epi);
+}
+
+template <int RL, int NI, int NIP>
+static hipError_t gather_shape(const GatherArgs &a, hipStream_t st) {
+    constexpr int D = ring_depth<NI, 1>();
+    auto k = k_fo_gather<RL, NI, NIP, xreg_fits<FMT_MXFP4, NI>()>;
+    const size_t lds = (size_t)a.K * 2;
+    const int planes = a.M * a.topk;
+    // the workgroups one launch over all planes' rows would use, per plane
+    const int g = grid_for(k, lds, (long)a.N * planes, RL, D, stream_per_cu<NI, 1>());
+    const int gx = (g + planes - 1) / planes;
+    hipLaunchKernelGGL(k, dim3(gx, planes), dim3(kBlock), lds, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fo_gather(const GatherArgs &a, hipStream_t st) {
+    LaneShape sh;
+    if (!pick_shape_rows(a.K / 32, (long)a.N * a.M * a.topk, sh)) return hipErrorInvalidValue;
+    QMV_SHAPE_SWITCH(gather_shape, a, st)
+}
+
 // Activation rows per argmax workgroup chunk, and the number of chunks.
 static void argmax_chunks(int M, int K, int mcw, int &mc, int &gy) {
     mc = (M > 1 && wide_fits(K, 1, mcw)) ? mcw : 1;

@@ -70,6 +70,18 @@ struct QkvArgs {
 
 hipError_t launch_fo_qkv(const QkvArgs &a, hipStream_t stream);
 
+// Expert-gather MXFP4 matvec: y[m][j] = the fixed-order matvec of x[m] with
+// expert idx[m][j]; experts are [E][N][K/2] weights + [E][N][K/32] scales.
+struct GatherArgs {
+    const uint8_t *wq, *e8m0;
+    const uint16_t *x;
+    const int32_t *idx;  // [M][topk]
+    void *y;             // [M][topk][N]
+    int y_dtype, E, topk, M, N, K;
+};
+
+hipError_t launch_fo_gather(const GatherArgs &a, hipStream_t stream);
+
 struct ArgmaxArgs {
     const uint32_t *wq;
     const uint16_t *scale, *x;
