@@ -437,6 +437,8 @@ __device__ __forceinline__ void store_out(void *y, size_t idx, float v, int dtyp
 // (uniform): 0 fp32, 1 fp16, 2 bf16; the buffer holds `elems` elements
 // (elems times the element size must stay below 4 GiB).
 constexpr uint32_t kStoreOob = 0xFFFFFFF0u;
+// The same offset on a buffer load returns zeros without touching memory.
+constexpr uint32_t kLoadOob = 0xFFFFFFF0u;
 struct OutBuf {
     __amdgpu_buffer_rsrc_t r;
     int dtype;

@@ -40,7 +40,9 @@ bool pick_shape(int nseg, LaneShape &s) {
     else if (nseg <= 24) s = {8, 3, 4};
     else if (nseg <= 32) s = {32, 1, 1};
     else if (nseg <= 64) s = {64, 1, 1};
-    else if (nseg <= 128) s = {32, 4, 4};  // two rows per wave: half the tree and epilogue work per row
+    // two rows per wave: half the tree and epilogue work per row
+    else if (nseg <= 96) s = {32, 3, 4};
+    else if (nseg <= 128) s = {32, 4, 4};
     else if (nseg <= 192) s = {64, 3, 4};
     else if (nseg <= 256) s = {64, 4, 4};
     else if (nseg <= 512) s = {64, 8, 8};
@@ -256,10 +258,26 @@ struct FoEngine {
         sstep = (uint32_t)stride * R * RPG * srow;
     }
 
+    // Byte offset of slot i's load (weights: step 16, scales: step ssz) from
+    // `base`; a slot past the row end (j = q + RL*i >= nseg) gets an offset
+    // past the end of the buffer, so it reads zeros and costs no memory
+    // traffic (its value is the tree's +0 padding anyway).  With the lane
+    // layouts pick_shape chooses, every slot below kSureLive is inside the
+    // row for every lane, so only the last slots need the test.
+    static constexpr int kSureLive = NI == 1 ? 0 : (NI == 8 ? 4 : NI - 1);
+    __device__ __forceinline__ uint32_t slot_off(uint32_t base, int i, uint32_t step) const {
+        const uint32_t c = (uint32_t)(i * RL) * step;
+        if (i < kSureLive) return base + c;
+        // select the base, then add the constant, which then fits the load's
+        // immediate offset field: one v_cndmask per load and no add
+        uint32_t b = q + RL * i < nseg ? base : kLoadOob - c;
+        asm volatile("" : "+v"(b));
+        return b + c;
+    }
+
     // Issue the loads of the next unit in this wave's sequence into `sl`.
     // Loads are unconditional (the compiler can then count outstanding loads
-    // exactly); segments past a row's end read the next row's bytes, which
-    // are never used.
+    // exactly); slots past a row's end load zeros (slot_off).
     __device__ __forceinline__ void load(RowSlot<F, NI, NMAT, R> &sl) {
         constexpr uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);
 #pragma unroll
@@ -272,13 +290,11 @@ struct FoEngine {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     sl.w[t][r][i] = __builtin_bit_cast(
-                        u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[t], wo + (uint32_t)(i * RL * 16), 0, kNT));
+                        u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[t], slot_off(wo, i, 16u), 0, kNT));
                     if constexpr (F == FMT_INT4)
-                        sl.seg[t][r][i] =
-                            __builtin_amdgcn_raw_buffer_load_b16(rsc[t], so + (uint32_t)(i * RL) * ssz, 0, 0);
+                        sl.seg[t][r][i] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], slot_off(so, i, ssz), 0, 0);
                     else if constexpr (F == FMT_MXFP4)
-                        sl.seg[t][r][i] =
-                            __builtin_amdgcn_raw_buffer_load_b8(rsc[t], so + (uint32_t)(i * RL) * ssz, 0, 0);
+                        sl.seg[t][r][i] = __builtin_amdgcn_raw_buffer_load_b8(rsc[t], slot_off(so, i, ssz), 0, 0);
                 }
             }
         woff += wstep;
@@ -293,12 +309,11 @@ struct FoEngine {
         for (int t = 0; t < NMAT; ++t) {
             if constexpr (F == FMT_INT2)
                 if (i == 0) s.rs[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff, 0, 0);
-            s.w[t] = __builtin_bit_cast(u4_t,
-                                        __builtin_amdgcn_raw_buffer_load_b128(rw[t], woff + (uint32_t)(i * RL * 16), 0, kNT));
+            s.w[t] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[t], slot_off(woff, i, 16u), 0, kNT));
             if constexpr (F == FMT_INT4)
-                s.sb[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff + (uint32_t)(i * RL) * ssz, 0, 0);
+                s.sb[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], slot_off(soff, i, ssz), 0, 0);
             else if constexpr (F == FMT_MXFP4)
-                s.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(rsc[t], soff + (uint32_t)(i * RL) * ssz, 0, 0);
+                s.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(rsc[t], slot_off(soff, i, ssz), 0, 0);
         }
         if (i == NI - 1) {
             woff += wstep;
@@ -1080,6 +1095,7 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
     case 834: return FN<8, 3, 4>(__VA_ARGS__);                              \
     case 3211: return FN<32, 1, 1>(__VA_ARGS__);                            \
     case 6411: return FN<64, 1, 1>(__VA_ARGS__);                            \
+    case 3234: return FN<32, 3, 4>(__VA_ARGS__);                            \
     case 3244: return FN<32, 4, 4>(__VA_ARGS__);                            \
     case 6434: return FN<64, 3, 4>(__VA_ARGS__);                            \
     case 6444: return FN<64, 4, 4>(__VA_ARGS__);                            \

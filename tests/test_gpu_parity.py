@@ -120,9 +120,9 @@ def test_workload5_mxfp4_sampled_rows(M):
 # ------------------------------------------------- shapes and lane layouts ----
 
 # K values covering every lane layout (segments per row: 1..8, ..16, ..24, ..32,
-# ..64, ..128, ..192, ..256, ..512) with ragged segment counts inside buckets.
-K_INT2 = [64, 320, 704, 1344, 1536, 1792, 2048, 3456, 4096, 7488, 8192, 9280, 12288, 16000, 16384]
-K_32 = [32, 160, 512, 544, 768, 992, 2016, 4096, 5376, 6144, 8000, 8192, 12352, 16384]
+# ..64, ..96, ..128, ..192, ..256, ..512) with ragged segment counts inside buckets.
+K_INT2 = [64, 320, 704, 1344, 1536, 1792, 2048, 3456, 4096, 5056, 6144, 7488, 8192, 9280, 12288, 16000, 16384]
+K_32 = [32, 160, 512, 544, 768, 992, 2016, 2112, 2880, 3072, 4096, 5376, 6144, 8000, 8192, 12352, 16384]
 
 
 @pytest.mark.parametrize("fmt", ["int2", "int4", "mxfp4"])
