@@ -239,6 +239,33 @@ __device__ __forceinline__ void segment_sums(const u4_t (&w)[NS], const DecodeCo
 }
 
 
+// MXFP4 inner step with the activations already in fp32 (bf16 widens
+// exactly): for the NS segments, t[a] = t[a] (+) e2m1_k * x_k for k ascending,
+// one fused multiply-add per code.  XF(a, k) returns activation k of segment
+// a as a float.  Byte b of word q holds elements 8q+2b (low nibble) and
+// 8q+2b+1 (high nibble).
+template <int NS, class XF>
+__device__ __forceinline__ void mx_sums_f32(const u4_t (&w)[NS], XF &&xf, float (&t)[NS][1]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f2_t c[NS][4];
+#pragma unroll
+        for (int a = 0; a < NS; ++a) {
+            c[a][0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[a][q], 1.0f, 0);
+            c[a][1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[a][q], 1.0f, 1);
+            c[a][2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[a][q], 1.0f, 2);
+            c[a][3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[a][q], 1.0f, 3);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int a = 0; a < NS; ++a) {
+                const float cv = (i & 1) ? c[a][i >> 1].y : c[a][i >> 1].x;
+                t[a][0] = __builtin_fmaf(cv, xf(a, 8 * q + i), t[a][0]);
+            }
+    }
+}
+
 // Inner step for one segment of R rows (the same segment index of R
 // different rows) and MC activation columns read from LDS:
 //   t[r][m] = t[r][m] (+) value[r]_k * x[m][k]   for k ascending over the segment.

@@ -26,6 +26,9 @@ namespace qmv {
 #ifndef QMV_MAX_GRID
 #define QMV_MAX_GRID 1024
 #endif
+#ifndef QMV_MX_XF32
+#define QMV_MX_XF32 1
+#endif
 #ifndef QMV_XREG_BUDGET
 #define QMV_XREG_BUDGET 96
 #endif
@@ -364,16 +367,31 @@ struct FoEngine {
         return fo_tree<RL, NIP>(v, P2);
     }
 
+    // MXFP4 with the activation slice in registers holds it widened to fp32
+    // (twice the registers): the inner step is then one conversion per two
+    // codes and one fused multiply-add per code, with no per-code widening.
+    static constexpr bool kXf32 = F == FMT_MXFP4 && XREG && QMV_MX_XF32;
+
     template <class Epi>
     __device__ __forceinline__ void run_stream(const uint16_t *xs, Epi &epi) {
         const DecodeConsts kc;
-        u4_t xr[XREG ? NI : 1][XREG ? XV : 1];
+        u4_t xr[XREG && !kXf32 ? NI : 1][XREG && !kXf32 ? XV : 1];
+        float xw[kXf32 ? NI : 1][kXf32 ? CODES : 1];
         int xoff[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int j = q + RL * i;
             xoff[i] = (j < nseg ? j : nseg - 1) * CODES;
-            if constexpr (XREG) {
+            if constexpr (kXf32) {
+#pragma unroll
+                for (int v = 0; v < XV; ++v) {
+                    const u4_t p = (j < nseg) ? *reinterpret_cast<const u4_t *>(xs + j * CODES + 8 * v)
+                                              : u4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        xw[i][8 * v + e] = (e & 1) ? u2f(p[e >> 1] & 0xFFFF0000u) : u2f(p[e >> 1] << 16);
+                }
+            } else if constexpr (XREG) {
 #pragma unroll
                 for (int v = 0; v < XV; ++v)
                     xr[i][v] = (j < nseg) ? *reinterpret_cast<const u4_t *>(xs + j * CODES + 8 * v)
@@ -393,7 +411,10 @@ struct FoEngine {
                     if (u < total_units) {  // uniform across the wave
                         // keep the activations opaque to loop-invariant code
                         // motion (see the unit-ring path)
-                        if constexpr (XREG) {
+                        if constexpr (kXf32) {
+#pragma unroll
+                            for (int k = 0; k < CODES; ++k) asm volatile("" : "+v"(xw[i][k]));
+                        } else if constexpr (XREG) {
 #pragma unroll
                             for (int v = 0; v < XV; ++v) asm volatile("" : "+v"(xr[i][v]));
                         } else {
@@ -414,7 +435,9 @@ struct FoEngine {
 #pragma unroll
                                 for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(s.w[t][v]) : "v"(segdep));
                         }
-                        if constexpr (XREG)
+                        if constexpr (kXf32)
+                            mx_sums_f32<NMAT>(s.w, [&](int, int k) { return xw[i][k]; }, a);
+                        else if constexpr (XREG)
                             segment_sums<F, NMAT, 1>(s.w, kc, [&](int, int, int vv) { return xr[i][vv]; }, a);
                         else
                             segment_sums<F, NMAT, 1>(
