@@ -72,6 +72,18 @@ MUTANTS = [
      "h_out[k] = orc_f64_to_f16((double)orc_f16_to_f32(x[k]) + (double)orc_f16_to_f32(r[k]));",
      "h_out[k] = x[k];",
      (), P.check_rmsnorm_vs_fp64),
+    ("gather_ids_transposed",
+     "const int64_t e = idx[m * topk + j];",
+     "const int64_t e = idx[j * M + m];",
+     (), P.check_expert_gather),
+    ("gather_expert_stride",
+     "orc_qmm_mxfp4(wq + e * N * (K / 2), e8m0 + e * N * (K / 32), x + m * K,",
+     "orc_qmm_mxfp4(wq + e * N * (K / 2), e8m0 + e * (N - 1) * (K / 32), x + m * K,",
+     (), P.check_expert_gather),
+    ("qkv_k_not_normalised",
+     "orc_qmv_int2(wq_k, s_k, xn, yk, M, Nk, K, nthreads);",
+     "orc_qmv_int2(wq_k, s_k, h, yk, M, Nk, K, nthreads);",
+     (), P.check_qkv_composition),
     ("argmax_last_max",
      "if (y[m * N + n] > y[m * N + best]) best = n;",
      "if (y[m * N + n] >= y[m * N + best]) best = n;",
