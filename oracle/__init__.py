@@ -67,6 +67,9 @@ def _bind(lib):
         "orc_int2_rmsnorm_gateup_gelu": ([vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp,
                                           i64, i64, i64, i32], None),
         "orc_int2_argmax": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32], None),
+        "orc_ternary_value": ([C.c_uint, i32], i32),
+        "orc_pack_ternary": ([vp, i64, i64, vp], None),
+        "orc_qmv_ternary": ([vp, vp, vp, vp, i64, i64, i64, i32], None),
         "orc_qmm_mxfp4_gather": ([vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32], None),
         "orc_int2_rmsnorm_qkv": ([vp, vp, vp, vp, f32, vp, vp, i64, vp, vp, i64, vp, vp, i64,
                                   vp, vp, vp, i64, i64, i32], None),
@@ -128,6 +131,33 @@ def qmm_mxfp4(wq, e8m0, x, threads=None, lib=None):
     assert wq.shape[1] * 2 == K and e8m0.shape == (N, K // 32) and K % 32 == 0
     y = np.empty((M, N), np.float32)
     lib.orc_qmm_mxfp4(_p(wq), _p(e8m0), _p(x), _p(y), M, N, K, threads or default_threads())
+    return y
+
+
+def ternary_row_bytes(K):
+    """Bytes per packed ternary row: ceil(K/80) segments of 16 bytes (80 codes)."""
+    return (K + 79) // 80 * 16
+
+
+def pack_ternary(v, lib=None):
+    """int8 values [N][K] in {-1,0,1} -> packed uint8 [N][ternary_row_bytes(K)]."""
+    lib = lib or load()
+    v = _c(v, np.int8)
+    N, K = v.shape
+    out = np.empty((N, ternary_row_bytes(K)), np.uint8)
+    lib.orc_pack_ternary(_p(v), N, K, _p(out))
+    return out
+
+
+def qmv_ternary(wq, scale, x, threads=None, lib=None):
+    """FO ternary matvec: wq uint8 [N][ternary_row_bytes(K)], scale fp16 bits [N],
+    x fp16 bits [M][K] -> y fp32 [M][N]."""
+    lib = lib or load()
+    wq, scale, x = _c(wq, np.uint8), _c(scale, np.uint16), _c(x, np.uint16)
+    N, (M, K) = wq.shape[0], x.shape
+    assert wq.shape[1] == ternary_row_bytes(K) and scale.shape == (N,)
+    y = np.empty((M, N), np.float32)
+    lib.orc_qmv_ternary(_p(wq), _p(scale), _p(x), _p(y), M, N, K, threads or default_threads())
     return y
 
 

@@ -197,6 +197,34 @@ ORC_API float orc_e2m1_value(unsigned nib)
     return (nib & 8u) ? -m : m;
 }
 
+/* Ternary ([PB] next-target ranking table, BitCPM ternary row: ternary
+ * unpack in the same family as the int2 byte decode).  Five base-3 digits per
+ * byte: b = t0 + 3 t1 + 9 t2 + 27 t3 + 81 t4, t_i in {0,1,2}, weight value
+ * t_i - 1.  Digit i is floor(b / 3^i) mod 3.  Bytes 243..255 are not codes. */
+ORC_API int orc_ternary_value(unsigned b, int i)
+{
+    unsigned d = b & 255u;
+    for (int s = 0; s < i; ++s) d /= 3u;
+    return (int)(d % 3u) - 1;
+}
+
+/* Pack values v[N][K] in {-1,0,1} into rows of ceil(K/80) 16-byte segments:
+ * element k is digit k mod 5 of byte k/5; digits past K are 1 (value 0). */
+ORC_API void orc_pack_ternary(const int8_t *v, int64_t N, int64_t K, uint8_t *wq)
+{
+    int64_t rb = (K + 79) / 80 * 16;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t c = 0; c < rb; ++c) {
+            unsigned b = 0, p = 1;
+            for (int i = 0; i < 5; ++i, p *= 3u) {
+                int64_t k = 5 * c + i;
+                int t = k < K ? v[n * K + k] + 1 : 1;
+                b += (unsigned)t * p;
+            }
+            wq[n * rb + c] = (uint8_t)b;
+        }
+}
+
 /* E8M0 scale: 2^(E-127); E = 255 encodes NaN. */
 ORC_API float orc_e8m0_value(uint8_t e)
 {
@@ -335,6 +363,26 @@ static float fo_mxfp4_row(const uint8_t *row, const uint8_t *erow, const float *
     return fo_tree(v, nseg);
 }
 
+/* Ternary: a row is ceil(K/80) 16-byte segments of 80 codes; only codes
+ * k < K are summed (the last segment may hold fewer); fp16 row scale at the
+ * end, as for int2. */
+static float fo_ternary_row(const uint8_t *row, float scale, const float *xf, int64_t K, float *v)
+{
+    int nseg = (int)((K + 79) / 80);
+    for (int j = 0; j < nseg; ++j) {
+        float t = 0.0f;
+        int64_t end = 80 * (int64_t)j + 80 < K ? 80 * (int64_t)j + 80 : K;
+        for (int64_t k = 80 * (int64_t)j; k < end; ++k) {
+            float c = (float)orc_ternary_value(row[k / 5], (int)(k % 5));
+            float p = c * xf[k]; /* exact */
+            t = t + p;
+        }
+        v[j] = t;
+    }
+    float total = fo_tree(v, nseg);
+    return scale * total;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Row-parallel driver (rows are independent; the thread count never changes */
 /* any bit of the result).                                                   */
@@ -410,6 +458,20 @@ static void mxfp4_rows(void *p, int64_t n0, int64_t n1)
     free(v);
 }
 
+static void ternary_rows(void *p, int64_t n0, int64_t n1)
+{
+    mv_ctx *c = (mv_ctx *)p;
+    int64_t nseg = (c->K + 79) / 80;
+    float *v = (float *)malloc(sizeof(float) * (size_t)pow2_at_least((int)nseg));
+    const uint8_t *wq = (const uint8_t *)c->wq;
+    const uint16_t *s = (const uint16_t *)c->sc;
+    for (int64_t n = n0; n < n1; ++n)
+        for (int64_t m = 0; m < c->M; ++m)
+            c->y[m * c->N + n] = fo_ternary_row(wq + n * nseg * 16, orc_f16_to_f32(s[n]),
+                                                c->xf + m * c->K, c->K, v);
+    free(v);
+}
+
 static float *widen_f16(const uint16_t *x, int64_t cnt)
 {
     float *xf = (float *)malloc(sizeof(float) * (size_t)(cnt > 0 ? cnt : 1));
@@ -451,6 +513,16 @@ ORC_API void orc_qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_
     float *xf = widen_bf16(x, M * K);
     mv_ctx c = {wq, e8m0, xf, y, M, N, K};
     parallel_rows(mxfp4_rows, &c, N, nthreads);
+    free(xf);
+}
+
+/* Ternary: wq uint8 [N][ceil(K/80)*16], scale fp16 [N], x fp16 [M][K]. */
+ORC_API void orc_qmv_ternary(const uint8_t *wq, const uint16_t *scale, const uint16_t *x, float *y,
+                             int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    float *xf = widen_f16(x, M * K);
+    mv_ctx c = {wq, scale, xf, y, M, N, K};
+    parallel_rows(ternary_rows, &c, N, nthreads);
     free(xf);
 }
 

@@ -23,6 +23,8 @@ Workloads (the shapes the benchmark and the parity tests use):
   6  fused RMSNorm -> int2 q/k/v   M=1, N=2048+512+512, K=1536
   7  MXFP4 expert gather  M=1, E=32 experts, topk=4, N=5760, K=2880 (a gpt-oss-sized
                           MoE up/gate projection; ids drawn uniformly without repeats)
+  8  ternary matvec     M=1, N=16384, K=4096 (an 8B-class decoder projection), five
+                          base-3 digits per byte, per-row fp16 scales ~U(0.01,0.05)
 """
 import numpy as np
 
@@ -112,6 +114,17 @@ def qkv_inputs(M, Nq, Nk, Nv, K, workload=6, salt=0):
 
 def argmax_inputs(M, N, K, workload=4, salt=0):
     return int2_inputs(M, N, K, workload=workload, salt=salt)
+
+
+def ternary_inputs(M, N, K, workload=8, salt=0, scale_range=(0.01, 0.05)):
+    """Packed ternary rows uint8 [N][ceil(K/80)*16] with every byte uniform over the 243
+    base-3 codes (five independent digits, each uniform over {0,1,2}; digits past K
+    drawn the same way), per-row fp16 scales, fp16 x [M][K] ~N(0,1)."""
+    g = rng(workload, M, salt)
+    wq = g.integers(0, 243, size=(N, (K + 79) // 80 * 16), dtype=np.uint16).astype(np.uint8)
+    scale = f16_bits(g.uniform(*scale_range, size=N))
+    x = f16_bits(g.standard_normal((M, K)))
+    return dict(wq=wq, scale=scale, x=x)
 
 
 def expert_inputs(M, E, topk, N, K, workload=7, salt=0, exp_range=(-8, 2)):

@@ -438,6 +438,78 @@ def check_qkv_composition(lib):
             assert np.max(np.abs(y[m] - yd)) <= 2e-3 * np.max(np.abs(yd)) + 1e-3
 
 
+# ---------------------------------------------------------------- ternary --
+
+def _ternary_table():
+    # digits of every code from the encoding side: enumerate all digit tuples
+    # (t0..t4) and place each at the byte sum t_i 3^i it encodes to
+    import itertools
+    tab = np.full((256, 5), 99, np.int64)
+    for t in itertools.product(range(3), repeat=5):
+        tab[sum(d * 3 ** i for i, d in enumerate(t))] = t
+    return tab - 1  # weight values; rows 243..255 stay invalid (98)
+
+
+def _ternary_ref64(wq, scale, x, K):
+    tab = _ternary_table()
+    vals = tab[wq].reshape(wq.shape[0], -1)[:, :K].astype(np.float64)  # [N][K]
+    xd = x.view(np.float16).astype(np.float64)
+    s = scale.view(np.float16).astype(np.float64)
+    return (xd @ vals.T) * s, (np.abs(xd) @ np.abs(vals).T) * s
+
+
+def check_ternary_decode(lib):
+    tab = _ternary_table()
+    for b in range(243):
+        assert [lib.orc_ternary_value(b, i) for i in range(5)] == list(tab[b]), b
+    g = np.random.default_rng(61)
+    for K in (5, 80, 83, 4096):
+        v = g.integers(-1, 2, (3, K)).astype(np.int8)
+        wq = oracle.pack_ternary(v, lib=lib)
+        assert wq.shape == (3, oracle.ternary_row_bytes(K)) and wq.max() <= 242
+        got = tab[wq].reshape(3, -1)
+        assert np.array_equal(got[:, :K], v) and np.all(got[:, K:] == 0)
+
+
+def check_ternary_vs_fp64(lib):
+    g = np.random.default_rng(62)
+    for K in (16, 80, 88, 160, 600, 1536):
+        for M, N in ((1, 1), (2, 7), (3, 5)):
+            d = synth.ternary_inputs(M, N, K, salt=K + N)
+            x = synth.f16_bits(g.standard_normal((M, K)) * 4)
+            y = oracle.qmv_ternary(d["wq"], d["scale"], x, lib=lib)
+            y64, a = _ternary_ref64(d["wq"], d["scale"], x, K)
+            nseg = (K + 79) // 80
+            dd = 80 + (math.ceil(math.log2(nseg)) if nseg > 1 else 0)
+            bound = gamma(dd) * a * (1 + U32) + U32 * np.abs(y64) + 1e-12 * a
+            assert np.all(np.abs(y - y64) <= bound), (K, M, N)
+            if K % 80:  # digits past K are never read: redraw them, same bits
+                wq2 = d["wq"].copy().astype(np.int64)
+                full = -(-K // 5)  # first byte holding only digits past K
+                wq2[:, full:] = g.integers(0, 243, (N, wq2.shape[1] - full))
+                r = K % 5
+                if r:  # the byte holding digit K: keep its low r digits
+                    lo = wq2[:, K // 5] % 3 ** r
+                    wq2[:, K // 5] = lo + 3 ** r * g.integers(0, 3 ** (5 - r), N)
+                y2 = oracle.qmv_ternary(wq2.astype(np.uint8), d["scale"], x, lib=lib)
+                assert np.array_equal(y2.view(np.uint32), y.view(np.uint32)), K
+
+
+def check_ternary_closed_form(lib):
+    # every weight +1 (or every weight -1) and integer x: every partial sum is
+    # exact, so y = s * (+-sum x) exactly; power-of-two scales keep it exact
+    g = np.random.default_rng(63)
+    for K in (80, 400, 4096):
+        xi = g.integers(-6, 7, (2, K))
+        x = synth.f16_bits(xi.astype(np.float64))
+        s = np.ldexp(1.0, g.integers(-3, 3, 4))
+        for code, sign in ((242, 1), (0, -1)):
+            wq = np.full((4, oracle.ternary_row_bytes(K)), code, np.uint8)
+            y = oracle.qmv_ternary(wq, synth.f16_bits(s), x, lib=lib)
+            want = sign * xi.sum(axis=1)[:, None] * s[None, :]
+            assert np.array_equal(y.astype(np.float64), want)
+
+
 def check_expert_gather(lib):
     # closed form: expert e has every element 1.0 (E2M1 code 2) and every block
     # scale 2^e; with integer x the output is exactly 2^idx * sum(x), so each
@@ -507,5 +579,6 @@ ALL_CHECKS = [
     check_int2_vs_fp64, check_int4_vs_fp64, check_mxfp4_vs_fp64, check_integer_x_exact,
     check_single_segment_sequential, check_golden_order, check_threads_identical,
     check_exp_accuracy, check_gelu_accuracy, check_rmsnorm_vs_fp64, check_fused_composition,
-    check_qkv_composition, check_expert_gather, check_argmax_ties,
+    check_qkv_composition, check_expert_gather, check_ternary_decode, check_ternary_vs_fp64,
+    check_ternary_closed_form, check_argmax_ties,
 ]

@@ -84,6 +84,14 @@ MUTANTS = [
      "orc_qmv_int2(wq_k, s_k, xn, yk, M, Nk, K, nthreads);",
      "orc_qmv_int2(wq_k, s_k, h, yk, M, Nk, K, nthreads);",
      (), P.check_qkv_composition),
+    ("ternary_digit_order_reversed",
+     "for (int s = 0; s < i; ++s) d /= 3u;",
+     "for (int s = 0; s < 4 - i; ++s) d /= 3u;",
+     (), P.check_ternary_decode),
+    ("ternary_digit_index_shifted",
+     "float c = (float)orc_ternary_value(row[k / 5], (int)(k % 5));",
+     "float c = (float)orc_ternary_value(row[k / 5], (int)((k + 1) % 5));",
+     (), P.check_ternary_vs_fp64),
     ("argmax_last_max",
      "if (y[m * N + n] > y[m * N + best]) best = n;",
      "if (y[m * N + n] >= y[m * N + best]) best = n;",
