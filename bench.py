@@ -222,6 +222,21 @@ def sweep_cases():
                 M * topk * eb + M * K * 2 + M * topk * 4 + M * topk * N * 4, 2 * M * topk * N * K, "hbm"
         return b
 
+    def ternary_m(M):
+        # an 8B-class decoder projection with ternary weights (five base-3
+        # digits per byte, rows of 52 segments of 80 codes)
+        def b():
+            N, K = 16384, 4096
+            d = synth.ternary_inputs(M, N, K, workload=8)
+            wb = N * ((K + 79) // 80 * 16) + N * 2
+            cp = -(-COLD_BYTES // wb)
+            wq, sc = rotating(dev(d["wq"], "u8"), cp), rotating(dev(d["scale"], "f16"), cp)
+            x = dev(d["x"], "f16")
+            y = torch.empty((M, N), device="cuda")
+            return (lambda i: (lambda: q.qmv_ternary(wq[i % cp], sc[i % cp], x, y=y))), \
+                wb + M * K * 2 + M * N * 4, 2 * M * N * K, "hbm"
+        return b
+
     def argmax_c4(M):
         def b():
             d = synth.argmax_inputs(M, 262144, 1536, workload=4)
@@ -265,6 +280,7 @@ def sweep_cases():
         ("fused rmsnorm+int2 gate/up+gelu N=2x8192 K=1536 M=1", fused_c3),
         ("fused rmsnorm+int2 q/k/v N=2048+512+512 K=1536 M=1", qkv_f1),
         ("mxfp4 expert gather E=32 top-4 N=5760 K=2880 M=1", gather_f2(1)),
+        ("ternary N=16384 K=4096 M=1", ternary_m(1)),
         ("int2 lm_head+argmax N=262144 K=1536 M=1", argmax_c4(1)),
         ("int2 lm_head+argmax N=262144 K=1536 M=4", argmax_c4(4)),
         ("mxfp4 N=21504 K=5376 M=1", mxfp4_m(1)),

@@ -107,7 +107,8 @@ typedef enum qmv_op {
     QMV_OP_INT2_GATEUP = 3,
     QMV_OP_INT2_ARGMAX = 4,
     QMV_OP_INT2_QKV = 5,
-    QMV_OP_MXFP4_GATHER = 6
+    QMV_OP_MXFP4_GATHER = 6,
+    QMV_OP_TERNARY = 7
 } qmv_op;
 
 /* Version of this ABI (QMV_ABI_VERSION). */
@@ -161,6 +162,23 @@ qmv_status qmv_int4(const uint32_t *wq, const uint16_t *scales, const uint16_t *
 qmv_status qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_t *x, void *y,
                      qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
                      size_t ws_bytes, void *stream);
+
+/* Ternary matvec ("raw-Metal loop playbook", next-target ranking table: the
+ * ternary row, whose unpack is in the same ALU-bound family as the int2 byte
+ * decode).  Weights in {-1, 0, +1}, five per byte in base 3:
+ * byte = t0 + 3 t1 + 9 t2 + 27 t3 + 81 t4 with digits t_i in {0,1,2} and
+ * weight t_i - 1; element k of a row is digit k mod 5 of byte k/5.  A row is
+ * ceil(K/80) 16-byte segments (80 codes each); digits past K are ignored.
+ * Only the 243 bytes 0..242 are codes (others give unspecified results).
+ * Fixed order as for int2 with 80-code segments (the last one summing only
+ * codes k < K); the fp16 row scale multiplies the reduced total.
+ *  wq uint8 [N][ceil(K/80)*16] (16-byte aligned); scale fp16 [N];
+ *  x fp16 [M][K] (16-byte aligned); y as for qmv_int2.  K a multiple of 8,
+ *  K <= 16384.  Several activation rows run one workgroup row each (every row
+ *  streams the weights).  Mode: FIXED; no workspace. */
+qmv_status qmv_ternary(const uint8_t *wq, const uint16_t *scale, const uint16_t *x, void *y,
+                       qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
+                       size_t ws_bytes, void *stream);
 
 /* Residual-add + RMSNorm prologue folded into dual int2 gate/up matvecs with
  * a GELU(gate)*up epilogue, one dispatch ("What moved the needle": the

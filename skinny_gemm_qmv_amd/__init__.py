@@ -11,6 +11,7 @@ Tensor conventions (all on the GPU, contiguous, row-major):
   int4 weights  torch.int32 [N, K/8]
   MXFP4 weights torch.uint8 [N, K/2];  E8M0 scales torch.uint8 [N, K/32]
   MXFP4 experts torch.uint8 [E, N, K/2] and [E, N, K/32]; expert ids torch.int32
+  ternary       torch.uint8 [N, ternary_row_bytes(K)] (five base-3 digits per byte)
   fp16 tensors  torch.float16;  bf16 tensors torch.bfloat16
 """
 import ctypes as C
@@ -20,7 +21,7 @@ import torch
 
 __all__ = [
     "qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu", "qmv_int2_rmsnorm_qkv",
-    "qmv_int2_argmax", "qmm_mxfp4_gather", "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
+    "qmv_int2_argmax", "qmm_mxfp4_gather", "qmv_ternary", "ternary_row_bytes", "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
     "MODES", "OPS",
 ]
 
@@ -33,7 +34,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 MODES = {"fixed": 0, "splitk": 1, "mfma": 2}
-OPS = {"int2": 0, "int4": 1, "mxfp4": 2, "int2_gateup": 3, "int2_argmax": 4, "int2_qkv": 5, "mxfp4_gather": 6}
+OPS = {"int2": 0, "int4": 1, "mxfp4": 2, "int2_gateup": 3, "int2_argmax": 4, "int2_qkv": 5, "mxfp4_gather": 6, "ternary": 7}
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _vp, _i, _sz, _f = C.c_void_p, C.c_int, C.c_size_t, C.c_float
@@ -52,6 +53,7 @@ _SIGS = {
     "qmv_int2_argmax": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
     "qmv_int2_rmsnorm_qkv": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i,
                               _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
+    "qmv_ternary": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp], _i),
     "qmm_mxfp4_gather": ([_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -223,6 +225,22 @@ def qmv_int2_rmsnorm_qkv(x, residual, gamma, eps, wq_q, s_q, wq_k, s_k, wq_v, s_
         _ptr(wq_v), _ptr(s_v), wq_v.shape[0], _ptr(ys[0]), _ptr(ys[1]), _ptr(ys[2]),
         _DTYPES[y_dtype], M, K, _mode(mode), None, 0, _stream(stream)), "qmv_int2_rmsnorm_qkv")
     return ys[0], ys[1], ys[2]
+
+
+def ternary_row_bytes(K):
+    """Bytes of one packed ternary row: ceil(K/80) segments of 16 bytes."""
+    return (K + 79) // 80 * 16
+
+
+def qmv_ternary(wq, scale, x, y=None, y_dtype=torch.float32, mode="fixed", stream=None):
+    """Ternary matvec (see qmv.h).  wq uint8 [N, ternary_row_bytes(K)], scale fp16 [N],
+    x fp16 [M, K]."""
+    M, K = x.shape
+    N = wq.shape[0]
+    _req(wq, "wq", torch.uint8, (N, ternary_row_bytes(K)))
+    _req(scale, "scale", torch.float16, (N,))
+    _req(x, "x", torch.float16, (M, K))
+    return _matvec(_lib.qmv_ternary, "qmv_ternary", wq, scale, x, y, y_dtype, mode, None, stream, "ternary")
 
 
 def qmm_mxfp4_gather(wq, e8m0, x, idx, y=None, y_dtype=torch.float32, mode="fixed", stream=None):

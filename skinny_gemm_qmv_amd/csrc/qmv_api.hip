@@ -150,6 +150,21 @@ qmv_status qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_t *x, 
     return run_matvec(2, wq, e8m0, x, y, y_dtype, M, N, K, mode, workspace, ws_bytes, stream);
 }
 
+qmv_status qmv_ternary(const uint8_t *wq, const uint16_t *scale, const uint16_t *x, void *y,
+                       qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
+                       size_t ws_bytes, void *stream) {
+    (void)workspace; (void)ws_bytes;
+    if (!wq || !scale || !x || !y) return QMV_ERR_INVALID_ARG;
+    if (!valid_shape(M, N, K, 8) || !valid_dtype(y_dtype) || !valid_mode(mode)) return QMV_ERR_INVALID_ARG;
+    const uint64_t row_bytes = (uint64_t)(K + 79) / 80 * 16;
+    if ((uint64_t)N * row_bytes >= (1ull << 32) - (1ull << 16)) return QMV_ERR_UNSUPPORTED;
+    if ((uint64_t)M * (uint64_t)N * 4u >= (1ull << 32) - (1ull << 16)) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(y, dtype_size(y_dtype))) return QMV_ERR_ALIGNMENT;
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+    qmv::MatvecArgs a{3, wq, scale, x, y, (int)y_dtype, M, N, K};
+    return hip_status(qmv::launch_fo_matvec(a, static_cast<hipStream_t>(stream)));
+}
+
 qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *residual,
                                         uint16_t *residual_out, const uint16_t *gamma, float eps,
                                         const uint32_t *wq_gate, const uint16_t *s_gate,

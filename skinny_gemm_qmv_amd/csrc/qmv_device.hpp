@@ -24,13 +24,18 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
-enum Fmt : int { FMT_INT2 = 0, FMT_INT4 = 1, FMT_MXFP4 = 2 };
+enum Fmt : int { FMT_INT2 = 0, FMT_INT4 = 1, FMT_MXFP4 = 2, FMT_TERN = 3 };
 
 // Codes held by one 16-byte segment (one dwordx4 load) of a packed row.
 template <int F> struct SegCodes;
 template <> struct SegCodes<FMT_INT2> { static constexpr int v = 64; };
 template <> struct SegCodes<FMT_INT4> { static constexpr int v = 32; };
 template <> struct SegCodes<FMT_MXFP4> { static constexpr int v = 32; };
+template <> struct SegCodes<FMT_TERN> { static constexpr int v = 80; };
+
+// Formats with one fp16 scale per row, applied to the reduced total (int2,
+// ternary); the others scale every segment.
+template <int F> constexpr bool kRowScale = F == FMT_INT2 || F == FMT_TERN;
 
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -67,6 +72,7 @@ struct DecodeConsts {
     uint32_t magic;                // VGPR
     uint32_t m2[5];                // int2 field masks, fields i and i+8 at bits 2i / 2i+16
     uint32_t m4lo, m4hi, xor2;     // int4 masks, int2 bias flip
+    uint32_t m8;                   // ternary byte-pair mask
     __device__ __forceinline__ DecodeConsts() {
         magic = in_vgpr(kMagic1024);
         m2[0] = in_sgpr(0x00030003u);
@@ -77,6 +83,7 @@ struct DecodeConsts {
         m4lo = in_sgpr(0x000F000Fu);
         m4hi = in_sgpr(0x00F000F0u);
         xor2 = in_sgpr(0xAAAAAAAAu);
+        m8 = in_sgpr(0x00FF00FFu);
     }
 };
 
@@ -117,6 +124,38 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     return u2f((e << 23) | special);
 }
 
+// Ternary: one word holds four bytes of five base-3 digits each (byte c of
+// the word = codes 5c .. 5c+4 of its 20).  Decoded with packed fp16
+// arithmetic, two bytes per instruction, every step exact:
+//   e = b - 1 from the magic-number placement (1024 + b) - 1025;
+//   per digit i: r = round(e / 3) (an fma with fp16(1/3) onto the magic 1536
+//   rounds to the nearest integer; e/3 lies within 1/3 + 0.03 of the integer
+//   floor(b / 3^(i+1)), so the rounding is never close), the digit value
+//   t_i - 1 = e - 3r (exact), then e = r - 1 for the next digit; after four
+//   digits e itself is t_4 - 1 (for the 243 valid codes, b < 243).
+// c[2i] holds digit i of bytes 0 and 2 (low, high half), c[2i+1] digit i of
+// bytes 1 and 3.
+__device__ __forceinline__ void tern_decode_word(uint32_t w, const DecodeConsts &k, h2_t (&c)[10]) {
+    const h2_t bias = {(_Float16)-1025.0f, (_Float16)-1025.0f};
+    const h2_t third = {(_Float16)(1.0f / 3.0f), (_Float16)(1.0f / 3.0f)};
+    const h2_t mg = {(_Float16)1536.0f, (_Float16)1536.0f};
+    const h2_t m3 = {(_Float16)-3.0f, (_Float16)-3.0f};
+    const h2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    h2_t e[2];
+    e[0] = u2h2((w & k.m8) | k.magic) + bias;
+    e[1] = u2h2(((w >> 8) & k.m8) | k.magic) + bias;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const h2_t r = __builtin_elementwise_fma(e[p], third, mg) - mg;
+            c[2 * i + p] = __builtin_elementwise_fma(r, m3, e[p]);
+            e[p] = r - one;
+        }
+    c[8] = e[0];
+    c[9] = e[1];
+}
+
 // v_fma_mix_f32 with two fp16 sources taken from halves of packed
 // registers (AH / BH = 1 selects the high half) and an fp32 addend:
 // acc = acc (+) a*b with one rounding.  fp16 x fp16 products are exact in
@@ -135,6 +174,47 @@ __device__ __forceinline__ void mix_mac(float &acc, uint32_t a2, uint32_t b2) {
         asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
 }
 
+// Ternary inner step (80 codes per segment): for k = 0 .. 79 in order,
+// t[a][m] = t[a][m] (+) value_k * x[m][k]; the words are decoded as the
+// codes reach them and each 16-byte activation vector is fetched once.
+template <int NS, int MC, class XF>
+__device__ __forceinline__ void tern_sums(const u4_t (&w)[NS], const DecodeConsts &kc, XF &&xf,
+                                          float (&t)[NS][MC]) {
+    h2_t c[NS][10];
+    u4_t xa[NS][MC];
+#pragma unroll
+    for (int k = 0; k < 80; ++k) {
+        if (k % 20 == 0) {
+#pragma unroll
+            for (int a = 0; a < NS; ++a) tern_decode_word(w[a][k / 20], kc, c[a]);
+        }
+        if (k % 8 == 0) {
+#pragma unroll
+            for (int a = 0; a < NS; ++a)
+#pragma unroll
+                for (int m = 0; m < MC; ++m) xa[a][m] = xf(a, m, k / 8);
+        }
+        const int byte = (k % 20) / 5, dig = k % 5;
+        const int pair = 2 * dig + (byte & 1);
+        const bool wh = byte >= 2, xh = k & 1;
+#pragma unroll
+        for (int a = 0; a < NS; ++a) {
+            const uint32_t cp = __builtin_bit_cast(uint32_t, c[a][pair]);
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                const uint32_t xp = xa[a][m][(k & 7) >> 1];
+                if (wh) {
+                    if (xh) mix_mac<1, 1>(t[a][m], cp, xp);
+                    else mix_mac<1, 0>(t[a][m], cp, xp);
+                } else {
+                    if (xh) mix_mac<0, 1>(t[a][m], cp, xp);
+                    else mix_mac<0, 0>(t[a][m], cp, xp);
+                }
+            }
+        }
+    }
+}
+
 // Inner step for the NS segments a lane holds in one row group, for MC
 // activation columns:
 //   t[a][m] = t[a][m] (+) value_k * x[m][k]   for k ascending over segment a.
@@ -146,6 +226,10 @@ __device__ __forceinline__ void mix_mac(float &acc, uint32_t a2, uint32_t b2) {
 template <int F, int NS, int MC, class XF>
 __device__ __forceinline__ void segment_sums(const u4_t (&w)[NS], const DecodeConsts &kc, XF &&xf,
                                              float (&t)[NS][MC]) {
+    if constexpr (F == FMT_TERN) {
+        tern_sums<NS, MC>(w, kc, xf, t);
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if constexpr (F == FMT_INT2) {

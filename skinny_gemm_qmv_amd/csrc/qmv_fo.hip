@@ -91,20 +91,25 @@ struct XStage {
     u4_t v[kXpt];
     // Row m of the staged chunk is x[m0 + m][0 .. len); `ld` is the row
     // stride of x (len < ld when one K split is staged).
-    __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int M, int ld, int len, int m0) {
-        const int per_row = len / 8;
+    // Only the first `valid` values of a row exist in x (a row padded to whole
+    // segments); the rest of the staged row is zero.
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int M, int ld, int len, int m0,
+                                         int valid = -1) {
+        const int per_row = len / 8, vrow = (valid < 0 ? len : valid) / 8;
 #pragma unroll
         for (int r = 0; r < kXpt; ++r) {
             const int e = threadIdx.x + r * blockDim.x;
             v[r] = u4_t{0u, 0u, 0u, 0u};
             if (e < MC * per_row) {
                 const int m = MC == 1 ? 0 : e / per_row, kk = e - m * per_row;
-                if (m0 + m < M) v[r] = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * ld + 8 * kk);
+                if (m0 + m < M && kk < vrow)
+                    v[r] = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * ld + 8 * kk);
             }
         }
     }
     __device__ __forceinline__ void store(const uint16_t *__restrict__ x, uint16_t *xs, int M, int ld, int len,
-                                          int m0) {
+                                          int m0, int valid = -1) {
+        const int vrow = (valid < 0 ? len : valid) / 8;
         const int per_row = len / 8;
 #pragma unroll
         for (int r = 0; r < kXpt; ++r) {
@@ -114,7 +119,7 @@ struct XStage {
         for (int e = threadIdx.x + kXpt * blockDim.x; e < MC * per_row; e += blockDim.x) {
             const int m = MC == 1 ? 0 : e / per_row, kk = e - m * per_row;
             u4_t w = {0u, 0u, 0u, 0u};
-            if (m0 + m < M) w = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * ld + 8 * kk);
+            if (m0 + m < M && kk < vrow) w = *reinterpret_cast<const u4_t *>(x + (size_t)(m0 + m) * ld + 8 * kk);
             *reinterpret_cast<u4_t *>(xs + (size_t)m * len + 8 * kk) = w;
         }
     }
@@ -245,7 +250,7 @@ struct FoEngine {
         // scalar loop (no exec-masked control flow around the load ring)
         first = __builtin_amdgcn_readfirstlane(blk * kWaves + wave);
         // bytes of scale data per row
-        srow = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u * nseg_row : (uint32_t)nseg_row);
+        srow = kRowScale<F> ? 2u : (F == FMT_INT4 ? 2u * nseg_row : (uint32_t)nseg_row);
         const uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);  // bytes per scale
 #pragma unroll
         for (int t = 0; t < NMAT; ++t) {
@@ -256,7 +261,7 @@ struct FoEngine {
         }
         const uint32_t n0 = (uint32_t)first * R * RPG + rsub;
         woff = n0 * row_bytes + (uint32_t)(seg0 + q) * 16u;
-        soff = n0 * srow + (F == FMT_INT2 ? 0u : (uint32_t)(seg0 + q) * ssz);
+        soff = n0 * srow + (kRowScale<F> ? 0u : (uint32_t)(seg0 + q) * ssz);
         wstep = (uint32_t)stride * R * RPG * row_bytes;
         sstep = (uint32_t)stride * R * RPG * srow;
     }
@@ -289,7 +294,7 @@ struct FoEngine {
             for (int r = 0; r < R; ++r) {
                 const uint32_t wo = woff + (uint32_t)r * RPG * row_bytes;
                 const uint32_t so = soff + (uint32_t)r * RPG * srow;
-                if constexpr (F == FMT_INT2) sl.rs[t][r] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], so, 0, 0);
+                if constexpr (kRowScale<F>) sl.rs[t][r] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], so, 0, 0);
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     sl.w[t][r][i] = __builtin_bit_cast(
@@ -310,7 +315,7 @@ struct FoEngine {
         constexpr uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);
 #pragma unroll
         for (int t = 0; t < NMAT; ++t) {
-            if constexpr (F == FMT_INT2)
+            if constexpr (kRowScale<F>)
                 if (i == 0) s.rs[t] = __builtin_amdgcn_raw_buffer_load_b16(rsc[t], soff, 0, 0);
             s.w[t] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rw[t], slot_off(woff, i, 16u), 0, kNT));
             if constexpr (F == FMT_INT4)
@@ -336,7 +341,7 @@ struct FoEngine {
 
     // The scaled sum of one segment (the int2 row scale comes at the end).
     __device__ __forceinline__ float scaled(float t, uint32_t sbits) const {
-        if constexpr (F == FMT_INT2) return t;
+        if constexpr (kRowScale<F>) return t;
         else if constexpr (F == FMT_INT4) return seg_scale<F>(sbits) * t;
         else return t * seg_scale<F>(sbits);
     }
@@ -356,7 +361,7 @@ struct FoEngine {
         for (int a = 0; a < NIP; ++a) {
             float val = 0.0f;
             if (a < NI) {
-                if constexpr (F == FMT_INT2) val = seg[a];
+                if constexpr (kRowScale<F>) val = seg[a];
                 else if constexpr (F == FMT_INT4) val = seg_scale<F>(sbits[a]) * seg[a];
                 else val = seg[a] * seg_scale<F>(sbits[a]);
                 // segments past the row end are the tree's +0 padding
@@ -450,7 +455,7 @@ struct FoEngine {
 #pragma unroll
                         for (int t = 0; t < NMAT; ++t) {
                             val[t][i] = scaled(a[t][0], s.sb[t]);
-                            if (i == 0) rsb[t] = F == FMT_INT2 ? s.rs[t] : 0u;
+                            if (i == 0) rsb[t] = kRowScale<F> ? s.rs[t] : 0u;
                         }
                     }
                     // refill with the same segment of the unit NS segments on
@@ -608,7 +613,7 @@ struct StoreEpi {
         for (int m = 0; m < MC; ++m) {
             if (m0 + m < M) {  // uniform
                 float r = tot[0][m];
-                if constexpr (F == FMT_INT2)
+                if constexpr (kRowScale<F>)
                     if (!partial) r = s * r;
                 out.put(act, (uint32_t)((m0 + m) * N + n), r);
             }
@@ -628,19 +633,21 @@ __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict_
     extern __shared__ __align__(16) uint16_t xs[];
     constexpr int CODES = SegCodes<F>::v;
     const int m0 = blockIdx.y * MC;
-    const int nseg_row = K / CODES;
+    // a ternary row is padded to whole segments; codes past K meet x = 0
+    const int nseg_row = (K + CODES - 1) / CODES;
     const int seg0 = blockIdx.z * seg_split;
     const int nloc = nseg_row - seg0 < seg_split ? nseg_row - seg0 : seg_split;
     const int klen = nloc * CODES;
+    const int kval = K - seg0 * CODES < klen ? K - seg0 * CODES : klen;  // real activations staged
     const uint16_t *xz = x + (size_t)seg0 * CODES;
     const uint8_t *const w1[1] = {wq};
     const void *const s1[1] = {sc};
     FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG>()> eng(w1, s1, N, klen, seg0,
                                                                                        nseg_row);
     XStage<MC> xst;
-    xst.load(xz, M, K, klen, m0);
+    xst.load(xz, M, K, klen, m0, kval);
     eng.prefetch();
-    xst.store(xz, xs, M, K, klen, m0);
+    xst.store(xz, xs, M, K, klen, m0, kval);
     __syncthreads();
     StoreEpi<F, MC> epi{OutBuf(part == nullptr ? y : static_cast<void *>(part + (size_t)blockIdx.z * M * N),
                                (uint32_t)M * (uint32_t)N, part == nullptr ? y_dtype : 0),
@@ -1081,7 +1088,7 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
     constexpr int D = ring_depth<NI, 1>();
     constexpr int CODES = SegCodes<F>::v;
     const uint8_t *wq = reinterpret_cast<const uint8_t *>(a.wq);
-    const int seg_split = a.seg_split > 0 ? a.seg_split : a.K / CODES;
+    const int seg_split = a.seg_split > 0 ? a.seg_split : (a.K + CODES - 1) / CODES;
     const int S = a.splits > 0 ? a.splits : 1;
     const int klen = seg_split * CODES;  // activation values staged per column
     // workgroups along x for one split: sized as if the S splits were S*N rows
@@ -1095,13 +1102,16 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
         const size_t lds = (size_t)klen * 2;
         hipLaunchKernelGGL(k, dim3(gx(k, lds, D * QMV_ROWS1, stream_per_cu<NI, 1>()), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
                            a.N, a.K, seg_split, a.part);
-    } else if (wide_fits(klen, 1, mc_wide<NI>())) {
-        constexpr int MCW = mc_wide<NI>();
-        auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false>;
-        const size_t lds = (size_t)MCW * klen * 2;
-        const int gy = (a.M + MCW - 1) / MCW;
-        hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), gy, S), dim3(kBlock), lds, st, wq, a.sc, a.x,
-                           a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
+    } else if (F != FMT_TERN && wide_fits(klen, 1, mc_wide<NI>())) {
+        // (ternary has no several-column inner step: one activation row per workgroup)
+        if constexpr (F != FMT_TERN) {
+            constexpr int MCW = mc_wide<NI>();
+            auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false>;
+            const size_t lds = (size_t)MCW * klen * 2;
+            const int gy = (a.M + MCW - 1) / MCW;
+            hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), gy, S), dim3(kBlock), lds, st, wq, a.sc,
+                               a.x, a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
+        }
     } else {
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
         const size_t lds = (size_t)klen * 2;
@@ -1132,14 +1142,18 @@ template <int RL, int NI, int NIP>
 static hipError_t mv_int4(const MatvecArgs &a, hipStream_t st) { return fo_matvec_shape<FMT_INT4, RL, NI, NIP>(a, st); }
 template <int RL, int NI, int NIP>
 static hipError_t mv_mxfp4(const MatvecArgs &a, hipStream_t st) { return fo_matvec_shape<FMT_MXFP4, RL, NI, NIP>(a, st); }
+template <int RL, int NI, int NIP>
+static hipError_t mv_tern(const MatvecArgs &a, hipStream_t st) { return fo_matvec_shape<FMT_TERN, RL, NI, NIP>(a, st); }
 
 hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t st) {
-    const int codes = a.fmt == FMT_INT2 ? 64 : 32;
+    const int codes = a.fmt == FMT_INT2 ? 64 : (a.fmt == FMT_TERN ? 80 : 32);
     LaneShape sh;
-    if (!pick_shape_rows(a.seg_split > 0 ? a.seg_split : a.K / codes, (long)a.N * (a.splits > 0 ? a.splits : 1), sh))
+    if (!pick_shape_rows(a.seg_split > 0 ? a.seg_split : (a.K + codes - 1) / codes,
+                         (long)a.N * (a.splits > 0 ? a.splits : 1), sh))
         return hipErrorInvalidValue;
     if (a.fmt == FMT_INT2) { QMV_SHAPE_SWITCH(mv_int2, a, st) }
     if (a.fmt == FMT_INT4) { QMV_SHAPE_SWITCH(mv_int4, a, st) }
+    if (a.fmt == FMT_TERN) { QMV_SHAPE_SWITCH(mv_tern, a, st) }
     QMV_SHAPE_SWITCH(mv_mxfp4, a, st)
 }
 

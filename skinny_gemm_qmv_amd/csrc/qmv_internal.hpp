@@ -19,9 +19,9 @@ struct LaneShape {
 bool pick_shape(int nseg, LaneShape &s);
 
 struct MatvecArgs {
-    int fmt;            // 0 int2, 1 int4, 2 mxfp4
-    const void *wq;     // packed rows, 16 bytes per segment
-    const void *sc;     // int2: fp16 [N]; int4: fp16 [N][K/32]; mxfp4: uint8 [N][K/32]
+    int fmt;            // 0 int2, 1 int4, 2 mxfp4, 3 ternary
+    const void *wq;     // packed rows, 16 bytes per segment (ternary: rows padded to whole segments)
+    const void *sc;     // int2, ternary: fp16 [N]; int4: fp16 [N][K/32]; mxfp4: uint8 [N][K/32]
     const uint16_t *x;  // [M][K] fp16 or bf16
     void *y;            // [M][N]
     int y_dtype;

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu",
-                 "qmv_int2_argmax", "qmv_int2_rmsnorm_qkv", "qmm_mxfp4_gather", "qmv_workspace_size", "qmv_workspace_init",
+                 "qmv_int2_argmax", "qmv_int2_rmsnorm_qkv", "qmm_mxfp4_gather", "qmv_ternary", "qmv_workspace_size", "qmv_workspace_init",
                  "qmv_status_string", "qmv_last_hip_error", "qmv_abi_version", "qmv_fo_spec"):
         assert want in names
 
@@ -145,6 +145,20 @@ def test_gather_validation():
     assert call(M=256, topk=256) == UNSUP          # M*topk planes > 65535 (grid.y)
     assert call(M=64, topk=64, N=1 << 18) == UNSUP  # M*topk*N*4 >= 4 GiB
     assert call(N=1 << 19, K=16384) == UNSUP        # one expert >= 4 GiB
+
+
+def test_ternary_validation():
+    fn = q._lib.qmv_ternary
+    assert _mv(fn, wq=0) == INVALID
+    assert _mv(fn, K=12) == INVALID        # K a multiple of 8
+    assert _mv(fn, K=16392) == INVALID
+    assert _mv(fn, M=257) == INVALID
+    assert _mv(fn, dt=5) == INVALID
+    assert _mv(fn, wq=24) == ALIGN
+    assert _mv(fn, x=8) == ALIGN
+    assert _mv(fn, mode=1) == UNSUP
+    assert _mv(fn, mode=2) == UNSUP
+    assert _mv(fn, N=1 << 22, K=16384) == UNSUP  # packed weights >= 4 GiB
 
 
 def test_argmax_validation():
