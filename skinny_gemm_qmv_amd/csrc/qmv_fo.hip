@@ -186,6 +186,7 @@ struct FoEngine {
     static constexpr int RPG = 64 / RL;   // rows per wave per row group
 
     int N, K, nseg, P2, q, rsub, total_units, stride, first;
+    const uint8_t *tern_lut = nullptr;  // ternary: this lane's copy of the LDS byte table
     uint32_t row_bytes, srow;
     // Buffer descriptors (SGPRs) for the packed weights and their scales.
     // Raw buffer loads take a 32-bit per-lane offset and return zero for any
@@ -379,7 +380,8 @@ struct FoEngine {
 
     template <class Epi>
     __device__ __forceinline__ void run_stream(const uint16_t *xs, Epi &epi) {
-        const DecodeConsts kc;
+        DecodeConsts kc;
+        kc.lut = tern_lut;
         u4_t xr[XREG && !kXf32 ? NI : 1][XREG && !kXf32 ? XV : 1];
         float xw[kXf32 ? NI : 1][kXf32 ? CODES : 1];
         int xoff[NI];
@@ -482,7 +484,8 @@ struct FoEngine {
             run_stream(xs, epi);
             return;
         }
-        const DecodeConsts kc;
+        DecodeConsts kc;
+        kc.lut = tern_lut;
         // x slice of this lane: segments q + RL*i (zeros past the row end)
         u4_t xr[XREG ? NI : 1][XREG ? MC : 1][XREG ? XV : 1];
         if constexpr (XREG) {
@@ -648,6 +651,13 @@ __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict_
     xst.load(xz, M, K, klen, m0, kval);
     eng.prefetch();
     xst.store(xz, xs, M, K, klen, m0, kval);
+    if constexpr (F == FMT_TERN && QMV_TERN_LUT) {
+        // the byte table follows the staged activations (klen * 2 bytes, a
+        // multiple of 160); each lane reads copy lane % kTernCopies
+        uint8_t *lut = reinterpret_cast<uint8_t *>(xs) + (size_t)MC * klen * 2;
+        tern_fill_lut(lut);
+        eng.tern_lut = lut + (threadIdx.x % kTernCopies) * 16;
+    }
     __syncthreads();
     StoreEpi<F, MC> epi{OutBuf(part == nullptr ? y : static_cast<void *>(part + (size_t)blockIdx.z * M * N),
                                (uint32_t)M * (uint32_t)N, part == nullptr ? y_dtype : 0),
@@ -1096,10 +1106,12 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
         const int g = grid_for(k, lds, (long)a.N * S, RL, depth, per_cu);
         return (g + S - 1) / S;
     };
+    // ternary: the byte table shares the workgroup's LDS
+    constexpr size_t lut = (F == FMT_TERN && QMV_TERN_LUT) ? kTernLutBytes : 0;
     if (a.M == 1) {
         constexpr bool xreg = xreg_fits<F, NI>();
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, xreg>;
-        const size_t lds = (size_t)klen * 2;
+        const size_t lds = (size_t)klen * 2 + lut;
         hipLaunchKernelGGL(k, dim3(gx(k, lds, D * QMV_ROWS1, stream_per_cu<NI, 1>()), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
                            a.N, a.K, seg_split, a.part);
     } else if (F != FMT_TERN && wide_fits(klen, 1, mc_wide<NI>())) {
@@ -1114,7 +1126,7 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
         }
     } else {
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
-        const size_t lds = (size_t)klen * 2;
+        const size_t lds = (size_t)klen * 2 + lut;
         hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), a.M, S), dim3(kBlock), lds, st, wq, a.sc, a.x,
                            a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
     }
