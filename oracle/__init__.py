@@ -67,6 +67,9 @@ def _bind(lib):
         "orc_int2_rmsnorm_gateup_gelu": ([vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp,
                                           i64, i64, i64, i32], None),
         "orc_int2_argmax": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32], None),
+        "orc_quant_mxfp4_block": ([vp, vp, vp], None),
+        "orc_int2_rmsnorm_gateup_gelu_mxfp4": ([vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                                i32], None),
         "orc_ternary_value": ([C.c_uint, i32], i32),
         "orc_pack_ternary": ([vp, i64, i64, vp], None),
         "orc_qmv_ternary": ([vp, vp, vp, vp, i64, i64, i64, i32], None),
@@ -132,6 +135,45 @@ def qmm_mxfp4(wq, e8m0, x, threads=None, lib=None):
     y = np.empty((M, N), np.float32)
     lib.orc_qmm_mxfp4(_p(wq), _p(e8m0), _p(x), _p(y), M, N, K, threads or default_threads())
     return y
+
+
+def quant_mxfp4(v, lib=None):
+    """fp16 bits [R][32*B] -> (E2M1 codes uint8 [R][16*B], E8M0 uint8 [R][B]), one
+    block per 32 consecutive values of a row."""
+    lib = lib or load()
+    v = _c(v, np.uint16)
+    R, N = v.shape
+    assert N % 32 == 0
+    codes = np.empty((R, N // 2), np.uint8)
+    e = np.empty((R, N // 32), np.uint8)
+    for r in range(R):
+        for b in range(N // 32):
+            blk = np.ascontiguousarray(v[r, 32 * b:32 * b + 32])
+            cb = np.empty(16, np.uint8)
+            eb = np.empty(1, np.uint8)
+            lib.orc_quant_mxfp4_block(_p(blk), _p(cb), _p(eb))
+            codes[r, 16 * b:16 * b + 16] = cb
+            e[r, b] = eb[0]
+    return codes, e
+
+
+def int2_rmsnorm_gateup_gelu_mxfp4(x, residual, gamma, eps, wq_gate, s_gate, wq_up, s_up,
+                                   threads=None, lib=None):
+    """Fused gate/up with its fp16 output quantised to MXFP4 per 32-value block.
+    Returns (codes uint8 [M][N/2], e8m0 uint8 [M][N/32], residual_out fp16 bits [M][K])."""
+    lib = lib or load()
+    x, residual, gamma = _c(x, np.uint16), _c(residual, np.uint16), _c(gamma, np.uint16)
+    wq_gate, wq_up = _c(wq_gate, np.uint32), _c(wq_up, np.uint32)
+    s_gate, s_up = _c(s_gate, np.uint16), _c(s_up, np.uint16)
+    (M, K), N = x.shape, wq_gate.shape[0]
+    assert N % 32 == 0
+    codes = np.empty((M, N // 2), np.uint8)
+    e = np.empty((M, N // 32), np.uint8)
+    res = np.empty((M, K), np.uint16)
+    lib.orc_int2_rmsnorm_gateup_gelu_mxfp4(_p(x), _p(residual), _p(res), _p(gamma), float(eps), _p(wq_gate),
+                                           _p(s_gate), _p(wq_up), _p(s_up), _p(codes), _p(e), M, N, K,
+                                           threads or default_threads())
+    return codes, e, res
 
 
 def ternary_row_bytes(K):

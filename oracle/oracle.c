@@ -664,6 +664,64 @@ ORC_API void orc_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *res
     free(h); free(xn); free(g); free(u);
 }
 
+/* MXFP4 quantisation of one 32-value block (OCP Microscaling Formats v1.0,
+ * conversion to an MX format): the shared exponent is floor(log2(max |v|))
+ * minus 2, the exponent of E2M1's largest value; the E8M0 byte is that plus
+ * 127; each element is v / 2^shared rounded to the nearest E2M1 value, ties
+ * to the even code (mantissa bit 0), which also clamps everything from 5 up
+ * to 6.  The sign bit is v's (a value rounding to zero keeps it).  An
+ * all-zero block takes the E8M0 byte 0.  Inputs are fp16, finite.  Code k
+ * goes to the low nibble of byte k/2 for even k, the high nibble for odd k. */
+ORC_API void orc_quant_mxfp4_block(const uint16_t *v, uint8_t *codes, uint8_t *e8m0)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+        double a = fabs((double)orc_f16_to_f32(v[i]));
+        if (a > amax) amax = a;
+    }
+    int shared = -127;
+    if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex);   /* amax = f * 2^ex, f in [0.5, 1): floor(log2) = ex - 1 */
+        shared = ex - 1 - 2;
+    }
+    *e8m0 = (uint8_t)(shared + 127);
+    for (int i = 0; i < 32; i += 2) codes[i / 2] = 0;
+    for (int i = 0; i < 32; ++i) {
+        double x = (double)orc_f16_to_f32(v[i]);
+        double mag = ldexp(fabs(x), -shared); /* exact */
+        int best = 0;
+        for (int c = 1; c < 8; ++c) {
+            double dc = fabs(mag - (double)E2M1_MAG[c]), db = fabs(mag - (double)E2M1_MAG[best]);
+            if (dc < db || (dc == db && (c % 2) == 0)) best = c;
+        }
+        unsigned code = (unsigned)best | (signbit(x) ? 8u : 0u);
+        codes[i / 2] |= (uint8_t)(i % 2 == 0 ? code : code << 4);
+    }
+}
+
+/* Fused activation-and-quantize ("Gemma 4 Optimization with Agentic Kernel
+ * Engineering", "What it found": a fused activation-and-quantize kernel on
+ * MI355X): the fused gate/up output out = fp16(GELU(gate) * up) of
+ * orc_int2_rmsnorm_gateup_gelu, then each row's 32-value blocks quantised
+ * to MXFP4 for the next MXFP4 GEMM.  codes uint8 [M][N/2], e8m0 uint8
+ * [M][N/32]; N a multiple of 32. */
+ORC_API void orc_int2_rmsnorm_gateup_gelu_mxfp4(const uint16_t *x, const uint16_t *residual,
+                                                uint16_t *residual_out, const uint16_t *gamma, float eps,
+                                                const uint32_t *wq_gate, const uint16_t *s_gate,
+                                                const uint32_t *wq_up, const uint16_t *s_up,
+                                                uint8_t *codes, uint8_t *e8m0,
+                                                int64_t M, int64_t N, int64_t K, int nthreads)
+{
+    uint16_t *out = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(M * N));
+    orc_int2_rmsnorm_gateup_gelu(x, residual, residual_out, gamma, eps, wq_gate, s_gate, wq_up, s_up,
+                                 out, NULL, NULL, M, N, K, nthreads);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < N / 32; ++b)
+            orc_quant_mxfp4_block(out + m * N + 32 * b, codes + m * (N / 2) + 16 * b, e8m0 + m * (N / 32) + b);
+    free(out);
+}
+
 /* Shared-prologue q/k/v ([A19] "What moved the needle", dispatch-count
  * fusion: the residual-add RMSNorm folded into the next matvec's prologue,
  * and q/k/v in a single dispatch): the prologue above on each activation

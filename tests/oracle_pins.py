@@ -438,6 +438,81 @@ def check_qkv_composition(lib):
             assert np.max(np.abs(y[m] - yd)) <= 2e-3 * np.max(np.abs(yd)) + 1e-3
 
 
+# ------------------------------------------------------- MXFP4 quantiser --
+
+def _mx_quant_ref(v16):
+    # the conversion written another way: the block exponent from the
+    # power-of-two bracket of the maximum, and the element rounding as
+    # round-half-even in three fixed-step bands (step 1/2 below 2, 1 in
+    # [2, 4), 2 from 4), clamped to 6
+    v = v16.view(np.float16).astype(np.float64)
+    amax = np.max(np.abs(v))
+    if amax == 0:
+        e = -127
+    else:
+        e = 0
+        while 2.0 ** e > amax:
+            e -= 1
+        while 2.0 ** (e + 1) <= amax:
+            e += 1
+        e -= 2
+    q = np.abs(v) * 2.0 ** (-e)
+    r = np.where(q < 2, np.round(q * 2) / 2, np.where(q < 4, np.round(q), 2 * np.round(q / 2)))
+    r = np.minimum(r, 6.0)
+    mag = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    code = np.array([int(np.flatnonzero(mag == x)[0]) for x in r]) | np.where(np.signbit(v), 8, 0)
+    packed = (code[0::2] | (code[1::2] << 4)).astype(np.uint8)
+    return packed, np.uint8(e + 127)
+
+
+def _mx_blocks(g, nblk):
+    # random blocks over a wide exponent range, with exact ties and values
+    # at and past the clamp planted relative to the block maximum
+    blocks = []
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 7.5, 0.5, 3.0])
+    for b in range(nblk):
+        s = int(g.integers(-20, 12))
+        top = 2.0 ** s * g.choice([4.0, 5.0, 6.0, 7.0, 7.5, 4.5])
+        vals = g.uniform(-1, 1, 32) * top
+        k = int(g.integers(0, 12))
+        vals[1:1 + k] = g.choice(mids, k) * 2.0 ** (s - 2) * g.choice([-1, 1], k)
+        vals[0] = top
+        if b % 7 == 3:
+            vals[:] = 0.0
+            vals[5] = -0.0
+        if b % 7 == 5:
+            vals[:] = g.choice([-0.0, 0.0], 32)
+            vals[9] = 2.0 ** -24  # smallest fp16
+        g.shuffle(vals)
+        blocks.append(synth.f16_bits(vals))
+    return np.array(blocks)
+
+
+def check_quant_mxfp4(lib):
+    g = np.random.default_rng(71)
+    v = _mx_blocks(g, 400)
+    codes, e = oracle.quant_mxfp4(v, lib=lib)
+    for i in range(v.shape[0]):
+        rc, re = _mx_quant_ref(v[i])
+        assert e[i, 0] == re, (i, e[i, 0], re)
+        assert np.array_equal(codes[i], rc), i
+    # values already on the grid of their block come back exactly
+    for s in (-14, 0, 9):
+        vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6] * 4) * np.repeat([1, -1, 1, -1], 8) * 2.0 ** s
+        c, e = oracle.quant_mxfp4(synth.f16_bits(vals)[None, :], lib=lib)
+        back = np.array([lib.orc_e2m1_value(int((c[0, i // 2] >> (4 * (i % 2))) & 15)) for i in range(32)])
+        assert np.array_equal(back * 2.0 ** (int(e[0, 0]) - 127), vals)
+
+
+def check_fused_quant_composition(lib):
+    d = synth.fused_inputs(2, 96, 1536, salt=4)
+    args = (d["x"], d["residual"], d["gamma"], d["eps"], d["wq_gate"], d["s_gate"], d["wq_up"], d["s_up"])
+    codes, e, res = oracle.int2_rmsnorm_gateup_gelu_mxfp4(*args, lib=lib)
+    out, res2, _, _ = oracle.int2_rmsnorm_gateup_gelu(*args, lib=lib)
+    c2, e2 = oracle.quant_mxfp4(out, lib=lib)
+    assert np.array_equal(codes, c2) and np.array_equal(e, e2) and np.array_equal(res, res2)
+
+
 # ---------------------------------------------------------------- ternary --
 
 def _ternary_table():
@@ -580,5 +655,5 @@ ALL_CHECKS = [
     check_single_segment_sequential, check_golden_order, check_threads_identical,
     check_exp_accuracy, check_gelu_accuracy, check_rmsnorm_vs_fp64, check_fused_composition,
     check_qkv_composition, check_expert_gather, check_ternary_decode, check_ternary_vs_fp64,
-    check_ternary_closed_form, check_argmax_ties,
+    check_ternary_closed_form, check_quant_mxfp4, check_fused_quant_composition, check_argmax_ties,
 ]

@@ -92,6 +92,18 @@ MUTANTS = [
      "float c = (float)orc_ternary_value(row[k / 5], (int)(k % 5));",
      "float c = (float)orc_ternary_value(row[k / 5], (int)((k + 1) % 5));",
      (), P.check_ternary_vs_fp64),
+    ("mxfp4_quant_ties_to_odd",
+     "if (dc < db || (dc == db && (c % 2) == 0)) best = c;",
+     "if (dc < db || (dc == db && (c % 2) == 1)) best = c;",
+     (), P.check_quant_mxfp4),
+    ("mxfp4_quant_exponent_off_by_one",
+     "shared = ex - 1 - 2;",
+     "shared = ex - 2;",
+     (), P.check_quant_mxfp4),
+    ("mxfp4_quant_sign_dropped",
+     "unsigned code = (unsigned)best | (signbit(x) ? 8u : 0u);",
+     "unsigned code = (unsigned)best | (x < 0.0 ? 8u : 0u);",
+     (), P.check_quant_mxfp4),
     ("argmax_last_max",
      "if (y[m * N + n] > y[m * N + best]) best = n;",
      "if (y[m * N + n] >= y[m * N + best]) best = n;",
