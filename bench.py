@@ -184,6 +184,25 @@ def sweep_cases():
             x, r, gm, 1e-6, wg[i % cp], sg[i % cp], wu[i % cp], su[i % cp], out=out,
             residual_out=ro))), nb, 2 * 2 * 8192 * 1536, "hbm"
 
+    def fused_quant_f4():
+        # the fused workload with its output quantised to MXFP4 in the same
+        # dispatch (codes + E8M0 instead of fp16)
+        d = synth.fused_inputs(1, 8192, 1536, workload=3)
+        wb = 2 * (8192 * 1536 // 4 + 8192 * 2)
+        cp = -(-COLD_BYTES // wb)
+        wg, sg = rotating(dev(d["wq_gate"], "u32"), cp), rotating(dev(d["s_gate"], "f16"), cp)
+        wu, su = rotating(dev(d["wq_up"], "u32"), cp), rotating(dev(d["s_up"], "f16"), cp)
+        x, r, gm = dev(d["x"], "f16"), dev(d["residual"], "f16"), dev(d["gamma"], "f16")
+        codes = torch.empty((1, 4096), dtype=torch.uint8, device="cuda")
+        e8 = torch.empty((1, 256), dtype=torch.uint8, device="cuda")
+        ro = torch.empty((1, 1536), dtype=torch.float16, device="cuda")
+        ws = torch.empty(q.workspace_size("int2_gateup_mxfp4", 1, 8192, 1536), dtype=torch.uint8, device="cuda")
+        q.workspace_init(ws)
+        nb = wb + 3 * 1536 * 2 + 1536 * 2 + 4096 + 256
+        return (lambda i: (lambda: q.qmv_int2_rmsnorm_gateup_gelu_mxfp4(
+            x, r, gm, 1e-6, wg[i % cp], sg[i % cp], wu[i % cp], su[i % cp], codes=codes, e8m0=e8,
+            residual_out=ro, workspace=ws))), nb, 2 * 2 * 8192 * 1536, "hbm"
+
     def qkv_f1():
         # q/k/v shapes of a K=1536 decoder layer: 8 query heads and 2 key/value
         # heads of 256 (synthetic int2 weights, the fused workload's recipe)
@@ -278,6 +297,7 @@ def sweep_cases():
         ("int4 N=16384 K=4096 M=8", int4_m(8)),
         ("int4 N=16384 K=4096 M=16", int4_m(16)),
         ("fused rmsnorm+int2 gate/up+gelu N=2x8192 K=1536 M=1", fused_c3),
+        ("fused rmsnorm+int2 gate/up+gelu+mxfp4 quantise N=2x8192 K=1536 M=1", fused_quant_f4),
         ("fused rmsnorm+int2 q/k/v N=2048+512+512 K=1536 M=1", qkv_f1),
         ("mxfp4 expert gather E=32 top-4 N=5760 K=2880 M=1", gather_f2(1)),
         ("ternary N=16384 K=4096 M=1", ternary_m(1)),

@@ -108,7 +108,8 @@ typedef enum qmv_op {
     QMV_OP_INT2_ARGMAX = 4,
     QMV_OP_INT2_QKV = 5,
     QMV_OP_MXFP4_GATHER = 6,
-    QMV_OP_TERNARY = 7
+    QMV_OP_TERNARY = 7,
+    QMV_OP_INT2_GATEUP_MXFP4 = 8
 } qmv_op;
 
 /* Version of this ABI (QMV_ABI_VERSION). */
@@ -202,6 +203,34 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *resid
                                         const uint32_t *wq_up, const uint16_t *s_up,
                                         uint16_t *out, int M, int N, int K, qmv_mode mode,
                                         void *workspace, size_t ws_bytes, void *stream);
+
+/* Fused activation-and-quantize ("Gemma 4 Optimization with Agentic Kernel
+ * Engineering", "What it found": a fused activation-and-quantize kernel on
+ * MI355X): exactly qmv_int2_rmsnorm_gateup_gelu's fp16 output, quantised to
+ * MXFP4 per block of 32 consecutive n of a row, in the same dispatch, for
+ * the next MXFP4 GEMM.  Quantisation (OCP Microscaling Formats v1.0): the
+ * block's shared exponent is floor(log2(max |v|)) - 2 (E8M0 byte = that +
+ * 127; an all-zero block gets 0); each element v / 2^shared is rounded to
+ * the nearest E2M1 value, ties to the even code, clamped to +-6, sign kept;
+ * element 2j in the low nibble of byte j, 2j+1 in the high nibble (the
+ * layout qmm_mxfp4 reads).
+ *  Inputs as for qmv_int2_rmsnorm_gateup_gelu; codes uint8 [M][N/2], e8m0
+ *  uint8 [M][N/32]; N a multiple of 32.  Needs a workspace of
+ *  qmv_workspace_size(QMV_OP_INT2_GATEUP_MXFP4, M, N, K, FIXED) bytes
+ *  (256-byte aligned: per-block arrival counters and fp16 staging), zeroed
+ *  once by qmv_workspace_init; every call leaves the counters at zero.
+ *  Mode: FIXED. */
+qmv_status qmv_int2_rmsnorm_gateup_gelu_mxfp4(const uint16_t *x, const uint16_t *residual,
+                                              uint16_t *residual_out, const uint16_t *gamma, float eps,
+                                              const uint32_t *wq_gate, const uint16_t *s_gate,
+                                              const uint32_t *wq_up, const uint16_t *s_up, uint8_t *codes,
+                                              uint8_t *e8m0, int M, int N, int K, qmv_mode mode,
+                                              void *workspace, size_t ws_bytes, void *stream);
+
+/* The same MXFP4 quantisation on its own: v fp16 [M][N] (2-byte aligned) ->
+ * codes uint8 [M][N/2], e8m0 uint8 [M][N/32]; N a multiple of 32,
+ * M*N < 2^31. */
+qmv_status qmv_quant_mxfp4(const uint16_t *v, uint8_t *codes, uint8_t *e8m0, int M, int N, void *stream);
 
 /* Shared-prologue q/k/v ("What moved the needle", dispatch-count fusion:
  * the residual-add RMSNorm folded into the next matvec's prologue, and

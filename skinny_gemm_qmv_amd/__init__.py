@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu", "qmv_int2_rmsnorm_qkv",
-    "qmv_int2_argmax", "qmm_mxfp4_gather", "qmv_ternary", "ternary_row_bytes", "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
+    "qmv_int2_argmax", "qmm_mxfp4_gather", "qmv_ternary", "ternary_row_bytes",
+    "qmv_int2_rmsnorm_gateup_gelu_mxfp4", "qmv_quant_mxfp4", "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
     "MODES", "OPS",
 ]
 
@@ -34,7 +35,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 MODES = {"fixed": 0, "splitk": 1, "mfma": 2}
-OPS = {"int2": 0, "int4": 1, "mxfp4": 2, "int2_gateup": 3, "int2_argmax": 4, "int2_qkv": 5, "mxfp4_gather": 6, "ternary": 7}
+OPS = {"int2": 0, "int4": 1, "mxfp4": 2, "int2_gateup": 3, "int2_argmax": 4, "int2_qkv": 5, "mxfp4_gather": 6, "ternary": 7, "int2_gateup_mxfp4": 8}
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _vp, _i, _sz, _f = C.c_void_p, C.c_int, C.c_size_t, C.c_float
@@ -53,6 +54,9 @@ _SIGS = {
     "qmv_int2_argmax": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
     "qmv_int2_rmsnorm_qkv": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i,
                               _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
+    "qmv_int2_rmsnorm_gateup_gelu_mxfp4": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _i, _i, _i, _i, _vp, _sz, _vp], _i),
+    "qmv_quant_mxfp4": ([_vp, _vp, _vp, _i, _i, _vp], _i),
     "qmv_ternary": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp], _i),
     "qmm_mxfp4_gather": ([_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp], _i),
 }
@@ -202,6 +206,48 @@ def qmv_int2_rmsnorm_gateup_gelu(x, residual, gamma, eps, wq_gate, s_gate, wq_up
         _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(out), M, N, K, _mode(mode), _ptr(ws), wsb,
         _stream(stream)), "qmv_int2_rmsnorm_gateup_gelu")
     return out
+
+
+def qmv_int2_rmsnorm_gateup_gelu_mxfp4(x, residual, gamma, eps, wq_gate, s_gate, wq_up, s_up, codes=None,
+                                       e8m0=None, residual_out=None, mode="fixed", workspace=None,
+                                       stream=None):
+    """The fused gate/up output quantised to MXFP4 in the same dispatch (see qmv.h).
+    Returns (codes uint8 [M, N/2], e8m0 uint8 [M, N/32]).  A workspace (uint8,
+    workspace_size("int2_gateup_mxfp4", ...) bytes, zeroed once with workspace_init)
+    may be passed to avoid a per-call allocation."""
+    M, K = x.shape
+    N = wq_gate.shape[0]
+    _req(x, "x", torch.float16, (M, K))
+    _req(residual, "residual", torch.float16, (M, K))
+    _req(gamma, "gamma", torch.float16, (K,))
+    _req(wq_gate, "wq_gate", torch.int32, (N, K // 16))
+    _req(wq_up, "wq_up", torch.int32, (N, K // 16))
+    _req(s_gate, "s_gate", torch.float16, (N,))
+    _req(s_up, "s_up", torch.float16, (N,))
+    codes = torch.empty((M, N // 2), dtype=torch.uint8, device=x.device) if codes is None else \
+        _req(codes, "codes", torch.uint8, (M, N // 2))
+    e8m0 = torch.empty((M, N // 32), dtype=torch.uint8, device=x.device) if e8m0 is None else \
+        _req(e8m0, "e8m0", torch.uint8, (M, N // 32))
+    if residual_out is not None:
+        _req(residual_out, "residual_out", torch.float16, (M, K))
+    ws, wsb = _workspace("int2_gateup_mxfp4", M, N, K, mode, workspace)
+    _check(_lib.qmv_int2_rmsnorm_gateup_gelu_mxfp4(
+        _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps), _ptr(wq_gate),
+        _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(codes), _ptr(e8m0), M, N, K, _mode(mode), _ptr(ws), wsb,
+        _stream(stream)), "qmv_int2_rmsnorm_gateup_gelu_mxfp4")
+    return codes, e8m0
+
+
+def qmv_quant_mxfp4(v, codes=None, e8m0=None, stream=None):
+    """fp16 [M, N] -> MXFP4 (codes uint8 [M, N/2], e8m0 uint8 [M, N/32]) per 32-value block."""
+    M, N = v.shape
+    _req(v, "v", torch.float16, (M, N))
+    codes = torch.empty((M, N // 2), dtype=torch.uint8, device=v.device) if codes is None else \
+        _req(codes, "codes", torch.uint8, (M, N // 2))
+    e8m0 = torch.empty((M, N // 32), dtype=torch.uint8, device=v.device) if e8m0 is None else \
+        _req(e8m0, "e8m0", torch.uint8, (M, N // 32))
+    _check(_lib.qmv_quant_mxfp4(_ptr(v), _ptr(codes), _ptr(e8m0), M, N, _stream(stream)), "qmv_quant_mxfp4")
+    return codes, e8m0
 
 
 def qmv_int2_rmsnorm_qkv(x, residual, gamma, eps, wq_q, s_q, wq_k, s_k, wq_v, s_v, y_q=None, y_k=None,

@@ -84,6 +84,10 @@ void qmv_fo_spec(int *segment_bytes, int *tree_kind, int *inner_step) {
 }
 
 size_t qmv_workspace_size(qmv_op op, int M, int N, int K, qmv_mode mode) {
+    if (op == QMV_OP_INT2_GATEUP_MXFP4) {
+        if (mode != QMV_MODE_FIXED || !valid_shape(M, N, K, 64) || N % 32 != 0) return 0;
+        return qmv::gateup_mxfp4_workspace_bytes(M, N);
+    }
     if (op == QMV_OP_INT2_ARGMAX) {
         if (mode != QMV_MODE_FIXED || !valid_shape(M, N, K, 64)) return 0;
         return qmv::argmax_workspace_bytes(M, N, K);
@@ -184,6 +188,43 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *resid
     if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
     qmv::GateUpArgs a{x, residual, gamma, residual_out, eps, wq_gate, wq_up, s_gate, s_up, out, M, N, K};
     return hip_status(qmv::launch_fo_gateup(a, static_cast<hipStream_t>(stream)));
+}
+
+qmv_status qmv_int2_rmsnorm_gateup_gelu_mxfp4(const uint16_t *x, const uint16_t *residual,
+                                              uint16_t *residual_out, const uint16_t *gamma, float eps,
+                                              const uint32_t *wq_gate, const uint16_t *s_gate,
+                                              const uint32_t *wq_up, const uint16_t *s_up, uint8_t *codes,
+                                              uint8_t *e8m0, int M, int N, int K, qmv_mode mode,
+                                              void *workspace, size_t ws_bytes, void *stream) {
+    if (!x || !residual || !gamma || !wq_gate || !s_gate || !wq_up || !s_up || !codes || !e8m0)
+        return QMV_ERR_INVALID_ARG;
+    if (!valid_shape(M, N, K, 64) || N % 32 != 0 || !valid_mode(mode) || !(eps >= 0.0f))
+        return QMV_ERR_INVALID_ARG;
+    if (!fits_32bit(N, K, 4)) return QMV_ERR_UNSUPPORTED;
+    if ((uint64_t)M * (uint64_t)N * 2u >= (1ull << 32) - (1ull << 16)) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(wq_gate, 16) || !aligned(wq_up, 16) ||
+        !aligned(gamma, 2) || (residual_out && !aligned(residual_out, 2)))
+        return QMV_ERR_ALIGNMENT;
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+    const size_t need = qmv::gateup_mxfp4_workspace_bytes(M, N);
+    if (!workspace || ws_bytes < need) return QMV_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QMV_ERR_ALIGNMENT;
+    const size_t cnt_bytes = ((size_t)M * (N / 32) * 4 + 255) / 256 * 256;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    qmv::GateUpArgs a{x, residual, gamma, residual_out, eps, wq_gate, wq_up, s_gate, s_up,
+                      reinterpret_cast<uint16_t *>(ws + cnt_bytes), M, N, K};
+    a.qcodes = codes;
+    a.qscale = e8m0;
+    a.qcnt = reinterpret_cast<uint32_t *>(ws);
+    return hip_status(qmv::launch_fo_gateup(a, static_cast<hipStream_t>(stream)));
+}
+
+qmv_status qmv_quant_mxfp4(const uint16_t *v, uint8_t *codes, uint8_t *e8m0, int M, int N, void *stream) {
+    if (!v || !codes || !e8m0) return QMV_ERR_INVALID_ARG;
+    if (M < 1 || N < 32 || N % 32 != 0) return QMV_ERR_INVALID_ARG;
+    if ((uint64_t)M * (uint64_t)N >= (1ull << 31)) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(v, 2)) return QMV_ERR_ALIGNMENT;
+    return hip_status(qmv::launch_quant_mxfp4(v, codes, e8m0, M, N, static_cast<hipStream_t>(stream)));
 }
 
 qmv_status qmv_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uint16_t *residual_out,

@@ -654,6 +654,32 @@ struct OutBuf {
     }
 };
 
+// MXFP4 quantisation of one 32-value block per 32-lane half of the wave
+// (OCP MX v1.0 conversion): lane l of the half holds element l as fp16 bits.
+// The shared exponent is floor(log2(max |v|)) - 2 (2 = the exponent of
+// E2M1's largest value 6): for a normal fp32 max with biased exponent ex the
+// E8M0 byte is ex - 2 and 2^-shared has the exponent field 256 - ex; an
+// all-zero block takes the byte 0.  v * 2^-shared is exact (|q| < 8) and the
+// hardware conversion rounds it to E2M1 (nearest, ties to even, clamped to
+// 6, sign kept).  Element 2j goes to the low nibble of byte j, 2j+1 to the
+// high nibble.  Every lane of the wave must call this (cross-lane reads);
+// only halves with `store` set write.
+__device__ __forceinline__ void mx_quant_half(uint16_t h, bool store, uint8_t *codes, uint8_t *scale) {
+    const int l = threadIdx.x & 31;
+    const float v = half_bits_to_f32(h);
+    float a = __builtin_fabsf(v);
+#pragma unroll
+    for (int s = 16; s >= 1; s >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, s, 32));
+    const uint32_t ex = f2u(a) >> 23;  // a >= 0, finite
+    const bool zero = !(a > 0.0f);
+    const float inv = u2f((256u - ex) << 23);
+    const float q = zero ? v : v * inv;
+    const float q_odd = __shfl_down(q, 1, 32);
+    const uint32_t b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q, q_odd, 1.0f, 0) & 0xFFu;
+    if (store && (l & 1) == 0) codes[l >> 1] = (uint8_t)b;
+    if (store && l == 0) *scale = (uint8_t)(zero ? 0u : ex - 2u);
+}
+
 // e^z for z in [-87, 87]: z = n ln2 + r (Cody & Waite: ln2 split into a
 // 15-significant-bit head, exact when multiplied by |n| <= 127, and a tail),
 // e^r by the degree-7 Taylor polynomial with binary32-rounded coefficients

@@ -184,6 +184,7 @@ struct FoEngine {
     static constexpr int CODES = SegCodes<F>::v;
     static constexpr int XV = CODES / 8;  // 16-byte activation vectors per segment per column
     static constexpr int RPG = 64 / RL;   // rows per wave per row group
+    static constexpr int kRowsPerUnit = R * RPG;
 
     int N, K, nseg, P2, q, rsub, total_units, stride, first;
     const uint8_t *tern_lut = nullptr;  // ternary: this lane's copy of the LDS byte table
@@ -853,15 +854,28 @@ struct RmsStage1 {
     }
 };
 
-template <int MC>
+// QM (quantised output): 0 none, the fp16 output goes to `out`; 1 the fp16
+// values go to this workgroup's LDS staging area (its 32-row blocks, see
+// mxfp4_local); 2 they go to `out` (the workspace staging area) for
+// mxfp4_tail.
+template <int MC, int QM = 0>
 struct GateUpEpi {
     OutBuf out;  // fp16 [M][N]
     int M, N, m0;
+    uint16_t *stage = nullptr;  // QM == 1: [slots][MC] fp16 bits
+    int bpr = 1;                // QM == 1: 32-row blocks per workgroup round
     __device__ __forceinline__ void operator()(int n, int q, const float (&tot)[2][MC],
                                                const float (&rs)[2]) {
         const float sg = rs[0];
         const float su = rs[1];
         const bool act = q == 0 && n < N;
+        int slot = 0;
+        if constexpr (QM == 1) {
+            // block b = n / 32 lies in round r = (b / bpr - blockIdx.x) / gridDim.x of this workgroup
+            const int b = n >> 5;
+            const int r = (b / bpr - (int)blockIdx.x) / (int)gridDim.x;
+            slot = (r * bpr + b % bpr) * 32 + (n & 31);
+        }
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
             if (m0 + m < M) {  // uniform
@@ -869,19 +883,78 @@ struct GateUpEpi {
                 const float u = su * tot[1][m];
                 const float ge = qmv_gelu(g);
                 const float o = ge * u;
-                out.put(act, (uint32_t)((m0 + m) * N + n), o);
+                if constexpr (QM == 1) {
+                    if (act) stage[slot * MC + m] = __builtin_bit_cast(uint16_t, to_f16(o));
+                } else {
+                    out.put(act, (uint32_t)((m0 + m) * N + n), o);
+                }
             }
         }
     }
 };
 
-template <int RL, int NI, int NIP, int MC, bool XREG>
+// Workgroup-local quantisation (QM == 1): with kWaves * (rows per unit) a
+// multiple of 32, round r of workgroup g covers the whole 32-row blocks
+// (g + r * G) * bpr + j, j < bpr (G workgroups), so after its last unit the
+// workgroup holds every value of its blocks in LDS and quantises them there:
+// no other workgroup is involved and nothing waits across the grid.
+template <int MC>
+__device__ __forceinline__ void mxfp4_local(const uint16_t *stage, int rounds, int bpr, uint8_t *qcodes,
+                                            uint8_t *qscale, int M, int N, int m0) {
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = N / 32, total = rounds * bpr * MC;
+    for (int t0 = 2 * wave; t0 < total; t0 += 2 * kWaves) {  // two blocks per wave
+        const int t = t0 + (lane >> 5);
+        const int m = t % MC, rj = t / MC;  // rj = r * bpr + j
+        const int b = ((int)blockIdx.x + (rj / bpr) * (int)gridDim.x) * bpr + rj % bpr;
+        const bool live = t < total && b < nb && m0 + m < M;
+        const uint16_t h = live ? stage[(rj * 32 + (lane & 31)) * MC + m] : (uint16_t)0;
+        const size_t row = live ? (size_t)(m0 + m) : 0;
+        mx_quant_half(h, live, qcodes + row * (N / 2) + (size_t)b * 16, qscale + row * nb + b);
+    }
+}
+
+// Fused activation-and-quantize ("Gemma 4 Optimization with Agentic Kernel
+// Engineering", "What it found"): after its units, a wave makes its fp16
+// outputs visible (release fence), then for every unit it produced and every
+// activation row adds one arrival to the unit's 32-row block.  The wave that
+// brings a block's count to 32 / (rows per unit) read all of it: it takes an
+// acquire fence, quantises the block from the staged fp16 values and resets
+// the counter to zero for the next call.  No wave waits for another.
+template <int MC, class Eng>
+__device__ __forceinline__ void mxfp4_tail(const Eng &eng, const uint16_t *stage, uint8_t *qcodes,
+                                           uint8_t *qscale, uint32_t *qcnt, int M, int N, int m0) {
+    constexpr uint32_t kArrivals = 32 / Eng::kRowsPerUnit;
+    const int lane = threadIdx.x & 63;
+    const int nblk = N / 32;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int u = eng.first; u < eng.total_units; u += eng.stride) {
+        const int blk = u * Eng::kRowsPerUnit / 32;
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            if (m0 + m >= M) break;  // uniform
+            const size_t c = (size_t)(m0 + m) * nblk + blk;
+            uint32_t old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(&qcnt[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (old != kArrivals - 1) continue;  // uniform
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            const uint16_t h = lane < 32 ? stage[(size_t)(m0 + m) * N + (size_t)blk * 32 + lane] : (uint16_t)0;
+            mx_quant_half(h, lane < 32, qcodes + (size_t)(m0 + m) * (N / 2) + (size_t)blk * 16,
+                          qscale + c);
+            if (lane == 0) __hip_atomic_store(&qcnt[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int RL, int NI, int NIP, int MC, bool XREG, int QM>
 __global__ __launch_bounds__(kBlock) void k_fo_gateup(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ residual,
     uint16_t *residual_out, const uint16_t *__restrict__ gamma, float eps,
     const uint32_t *__restrict__ wq_gate, const uint16_t *__restrict__ s_gate,
     const uint32_t *__restrict__ wq_up, const uint16_t *__restrict__ s_up, uint16_t *out, int M,
-    int N, int K) {
+    int N, int K, uint8_t *qcodes, uint8_t *qscale, uint32_t *qcnt, int qrounds) {
     extern __shared__ __align__(16) uint16_t smem[];
     uint16_t *xs = smem;  // [MC][K]: h, then overwritten in place by the normalised xn
     float *inv_s = reinterpret_cast<float *>(smem + (size_t)MC * K);
@@ -899,8 +972,18 @@ __global__ __launch_bounds__(kBlock) void k_fo_gateup(
         eng.prefetch();
         rmsnorm_prologue<MC>(x, residual, gamma, residual_out, eps, M, K, m0, xs, xs, inv_s);
     }
-    GateUpEpi<MC> epi{OutBuf(out, (uint32_t)M * (uint32_t)N, 1), M, N, m0};
+    using Eng = decltype(eng);
+    GateUpEpi<MC, QM> epi{OutBuf(out, (uint32_t)M * (uint32_t)N, 1), M, N, m0};
+    constexpr int kBpr = kWaves * Eng::kRowsPerUnit / 32;
+    uint16_t *stage = reinterpret_cast<uint16_t *>(inv_s + 16 * MC);  // after the prologue's scratch
+    if constexpr (QM == 1) {
+        static_assert((kWaves * Eng::kRowsPerUnit) % 32 == 0, "workgroup rounds must cover whole blocks");
+        epi.stage = stage;
+        epi.bpr = kBpr;
+    }
     eng.run(xs, epi);
+    if constexpr (QM == 1) mxfp4_local<MC>(stage, qrounds, kBpr, qcodes, qscale, M, N, m0);
+    if constexpr (QM == 2) mxfp4_tail<MC>(eng, out, qcodes, qscale, qcnt, M, N, m0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1169,38 +1252,94 @@ hipError_t launch_fo_matvec(const MatvecArgs &a, hipStream_t st) {
     QMV_SHAPE_SWITCH(mv_mxfp4, a, st)
 }
 
+// Launch one gate/up kernel variant: QM as in GateUpEpi; for QM == 1 the
+// LDS also holds the workgroup's staged outputs (rounds x blocks per round x
+// 32 x MC fp16 values).
+template <int RL, int NI, int NIP, int MC, bool XREG>
+static void gu_launch(const GateUpArgs &a, hipStream_t st, size_t lds, int depth, int per_cu, int gy) {
+    constexpr int R = rows_block<MC, XREG>();
+    constexpr int kRpu = R * (64 / RL);
+    constexpr bool local_ok = (kWaves * kRpu) % 32 == 0;
+    if (a.qcodes == nullptr) {
+        auto k = k_fo_gateup<RL, NI, NIP, MC, XREG, 0>;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, depth, per_cu), gy), dim3(kBlock), lds, st, a.x,
+                           a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up, a.s_up,
+                           a.out, a.M, a.N, a.K, nullptr, nullptr, nullptr, 0);
+    } else if constexpr (local_ok) {
+        constexpr int bpr = kWaves * kRpu / 32;
+        auto k = k_fo_gateup<RL, NI, NIP, MC, XREG, 1>;
+        // sized without the staging area first, then given it: the rounds
+        // depend on the grid and the staging is small
+        const int g = grid_for(k, lds, a.N, RL, depth, per_cu);
+        const long units = a.N / kRpu;
+        const int rounds = (int)((units + (long)g * kWaves - 1) / ((long)g * kWaves));
+        const size_t lds_q = lds + (size_t)rounds * bpr * 32 * MC * 2;
+        hipLaunchKernelGGL(k, dim3(g, gy), dim3(kBlock), lds_q, st, a.x, a.residual, a.residual_out, a.gamma,
+                           a.eps, a.wq_gate, a.s_gate, a.wq_up, a.s_up, a.out, a.M, a.N, a.K, a.qcodes,
+                           a.qscale, a.qcnt, rounds);
+    } else {
+        auto k = k_fo_gateup<RL, NI, NIP, MC, XREG, 2>;
+        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, depth, per_cu), gy), dim3(kBlock), lds, st, a.x,
+                           a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up, a.s_up,
+                           a.out, a.M, a.N, a.K, a.qcodes, a.qscale, a.qcnt, 0);
+    }
+}
+
 template <int RL, int NI, int NIP>
 static hipError_t gu_shape(const GateUpArgs &a, hipStream_t st) {
     constexpr int D = ring_depth<NI, 2>();
     constexpr int MCW = mc_wide<NI, 2>();
     if (a.M == 1 || !wide_fits(a.K, 1, MCW)) {
         const size_t lds = (size_t)a.K * 2 + 64;
-        if (a.M == 1) {
-            auto k = k_fo_gateup<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>;
-            hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, D, stream_per_cu<NI, 2>()), 1), dim3(kBlock), lds, st, a.x,
-                               a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
-                               a.s_up, a.out, a.M, a.N, a.K);
-        } else {
-            auto k = k_fo_gateup<RL, NI, NIP, 1, false>;
-            hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), a.M), dim3(kBlock), lds, st, a.x,
-                               a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
-                               a.s_up, a.out, a.M, a.N, a.K);
-        }
+        if (a.M == 1)
+            gu_launch<RL, NI, NIP, 1, xreg_fits<FMT_INT2, NI>()>(a, st, lds, D, stream_per_cu<NI, 2>(), 1);
+        else
+            gu_launch<RL, NI, NIP, 1, false>(a, st, lds, kWideUnits * QMV_ROWS, 0, a.M);
     } else {
-        auto k = k_fo_gateup<RL, NI, NIP, MCW, false>;
         const size_t lds = (size_t)MCW * a.K * 2 + 64 * MCW;
-        const int gy = (a.M + MCW - 1) / MCW;
-        hipLaunchKernelGGL(k, dim3(grid_for(k, lds, a.N, RL, kWideUnits * QMV_ROWS), gy), dim3(kBlock), lds, st, a.x,
-                           a.residual, a.residual_out, a.gamma, a.eps, a.wq_gate, a.s_gate, a.wq_up,
-                           a.s_up, a.out, a.M, a.N, a.K);
+        gu_launch<RL, NI, NIP, MCW, false>(a, st, lds, kWideUnits * QMV_ROWS, 0, (a.M + MCW - 1) / MCW);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_fo_gateup(const GateUpArgs &a, hipStream_t st) {
     LaneShape sh;
-    if (!pick_shape_rows(a.K / 64, a.N, sh)) return hipErrorInvalidValue;
+    const int nseg = a.K / 64;
+    if (a.qcodes != nullptr && nseg <= 24) {
+        // quantised output: eight lanes per row (eight rows per wave and unit),
+        // so that a workgroup's round covers whole 32-row blocks
+        sh = nseg <= 8 ? LaneShape{8, 1, 1} : LaneShape{8, 3, 4};
+    } else if (!pick_shape_rows(nseg, a.N, sh)) {
+        return hipErrorInvalidValue;
+    }
     QMV_SHAPE_SWITCH(gu_shape, a, st)
+}
+
+size_t gateup_mxfp4_workspace_bytes(int M, int N) {
+    const size_t cnt = ((size_t)M * (N / 32) * 4 + 255) / 256 * 256;
+    return cnt + (size_t)M * N * 2;
+}
+
+// Two blocks per wave (one per 32-lane half), grid-stride over wave pairs of
+// blocks so that every lane of a wave runs the same iterations.
+__global__ void k_quant_mxfp4(const uint16_t *__restrict__ v, uint8_t *codes, uint8_t *scale, int nblk) {
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * (blockDim.x >> 6);
+    for (int w = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); 2 * w < nblk; w += waves) {
+        const int b = 2 * w + (lane >> 5);
+        const bool live = b < nblk;
+        const uint16_t h = live ? v[(size_t)b * 32 + (lane & 31)] : (uint16_t)0;
+        mx_quant_half(h, live, codes + (size_t)b * 16, scale + b);
+    }
+}
+
+hipError_t launch_quant_mxfp4(const uint16_t *v, uint8_t *codes, uint8_t *scale, int M, int N,
+                              hipStream_t st) {
+    const int nblk = (int)((size_t)M * N / 32);
+    int g = (nblk + 7) / 8;  // 4 waves of 2 blocks per workgroup
+    if (g > 4096) g = 4096;
+    hipLaunchKernelGGL(k_quant_mxfp4, dim3(g), dim3(256), 0, st, v, codes, scale, nblk);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -50,11 +50,22 @@ struct GateUpArgs {
     float eps;
     const uint32_t *wq_gate, *wq_up;
     const uint16_t *s_gate, *s_up;
-    uint16_t *out;
+    uint16_t *out;  // fp16 [M][N] (with quantisation: the staging area in the workspace)
     int M, N, K;
+    // MXFP4 quantisation of out (all null: none): codes [M][N/2], E8M0
+    // [M][N/32], one arrival counter per block [M][N/32] (zero between calls)
+    uint8_t *qcodes = nullptr, *qscale = nullptr;
+    uint32_t *qcnt = nullptr;
 };
 
 hipError_t launch_fo_gateup(const GateUpArgs &a, hipStream_t stream);
+
+// Workspace of the quantising gate/up: counters, then the fp16 staging area.
+size_t gateup_mxfp4_workspace_bytes(int M, int N);
+
+// fp16 [M][N] -> MXFP4 codes [M][N/2] + E8M0 [M][N/32], N a multiple of 32.
+hipError_t launch_quant_mxfp4(const uint16_t *v, uint8_t *codes, uint8_t *scale, int M, int N,
+                              hipStream_t stream);
 
 // Shared-prologue q/k/v: index 0 = q, 1 = k, 2 = v.
 struct QkvArgs {

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu",
-                 "qmv_int2_argmax", "qmv_int2_rmsnorm_qkv", "qmm_mxfp4_gather", "qmv_ternary", "qmv_workspace_size", "qmv_workspace_init",
+                 "qmv_int2_argmax", "qmv_int2_rmsnorm_qkv", "qmm_mxfp4_gather", "qmv_ternary", "qmv_int2_rmsnorm_gateup_gelu_mxfp4", "qmv_quant_mxfp4", "qmv_workspace_size", "qmv_workspace_init",
                  "qmv_status_string", "qmv_last_hip_error", "qmv_abi_version", "qmv_fo_spec"):
         assert want in names
 
@@ -159,6 +159,39 @@ def test_ternary_validation():
     assert _mv(fn, mode=1) == UNSUP
     assert _mv(fn, mode=2) == UNSUP
     assert _mv(fn, N=1 << 22, K=16384) == UNSUP  # packed weights >= 4 GiB
+
+
+def test_gateup_mxfp4_validation():
+    fn = q._lib.qmv_int2_rmsnorm_gateup_gelu_mxfp4
+
+    def call(ptrs=None, M=1, N=64, K=64, mode=0, eps=1e-6, ws=None, wsb=0):
+        p = ptrs or {}
+        a = [P(p.get(i, 16)) if p.get(i, 16) else None for i in range(10)]
+        # x, residual, residual_out, gamma, wq_gate, s_gate, wq_up, s_up, codes, e8m0
+        return fn(a[0], a[1], a[2], a[3], C.c_float(eps), a[4], a[5], a[6], a[7], a[8], a[9], M, N, K, mode,
+                  P(ws) if ws else None, wsb, None)
+    assert call({0: 0}) == INVALID
+    assert call({8: 0}) == INVALID
+    assert call(N=48) == INVALID           # N a multiple of 32
+    assert call(K=96) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call({4: 24}) == ALIGN
+    assert call(mode=1) == UNSUP
+    assert call() == WS                    # workspace required
+    need = q._lib.qmv_workspace_size(8, 1, 64, 64, 0)
+    assert need == 256 + 64 * 2
+    assert call(ws=256, wsb=need - 2) == WS
+    assert call(ws=272, wsb=need) == ALIGN
+    assert q._lib.qmv_workspace_size(8, 1, 48, 64, 0) == 0
+
+
+def test_quant_mxfp4_validation():
+    fn = q._lib.qmv_quant_mxfp4
+    assert fn(None, P(16), P(16), 1, 64, None) == INVALID
+    assert fn(P(16), P(16), P(16), 1, 48, None) == INVALID
+    assert fn(P(16), P(16), P(16), 0, 64, None) == INVALID
+    assert fn(P(17), P(16), P(16), 1, 64, None) == ALIGN
+    assert fn(P(16), P(16), P(16), 1 << 16, 1 << 15, None) == UNSUP
 
 
 def test_argmax_validation():
