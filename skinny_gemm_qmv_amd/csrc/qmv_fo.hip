@@ -57,7 +57,13 @@ bool pick_shape(int nseg, LaneShape &s) {
 // over more lanes (fewer rows per wave, more waves) as long as at least half
 // of the row's lanes hold a segment.  The order of the sums does not depend
 // on the layout.
-constexpr long kFewRowGroups = 4096;
+// Measured: the fused gate/up at N=8192 (1024 row groups of eight rows)
+// runs 7.7 us widened to 32 lanes per row and 6.0 us as is; the int2 matvec
+// at N=2048 (256 row groups) 3.8 us as is and 3.0 us widened.
+#ifndef QMV_FEW_RG
+#define QMV_FEW_RG 1024
+#endif
+constexpr long kFewRowGroups = QMV_FEW_RG;
 
 bool pick_shape_rows(int nseg, long N, LaneShape &s) {
     if (!pick_shape(nseg, s)) return false;
