@@ -443,10 +443,68 @@ __device__ __forceinline__ void mx_sums_f32(const u4_t (&w)[NS], XF &&xf, float 
 // for all R rows.  The LDS offset is re-derived through an opaque copy at
 // every step so the reads stay next to their use (hoisting them makes the
 // compiler hold a whole segment of activations for every column).
+// Ternary several-column inner step: R rows (the same segment of R rows)
+// and MC activation columns read from LDS; each word is decoded once for all
+// MC columns and each activation vector is used for all R rows.  Codes run
+// in order k = 0 .. 79 in every (row, column) chain; the opaque offsets and
+// words follow the generic several-column step below.
+template <int R, int MC>
+__device__ __forceinline__ void tern_sums_rows(const u4_t (&w)[R], const DecodeConsts &kc, const uint16_t *xs,
+                                               int xo, int K, float (&t)[R][MC]) {
+    h2_t c[R][10];
+    u4_t xa[MC];
+    float dep = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 80; ++k) {
+        if (k % 20 == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                uint32_t wv = w[r][k / 20];
+                asm volatile("" : "+v"(wv) : "v"(dep));
+                tern_decode_word(wv, kc, c[r]);
+            }
+        }
+        if (k % 8 == 0) {
+            int o = xo + k;
+            asm volatile("" : "+v"(o) : "v"(dep));
+#pragma unroll
+            for (int m = 0; m < MC; ++m) xa[m] = *reinterpret_cast<const u4_t *>(xs + m * K + o);
+        }
+        const int byte = (k % 20) / 5, dig = k % 5;
+        const int pair = 2 * dig + (byte & 1);
+        const bool wh = byte >= 2, xh = k & 1;
+#pragma unroll
+        for (int m = 0; m < MC; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t cp = __builtin_bit_cast(uint32_t, c[r][pair]);
+                const uint32_t xp = xa[m][(k & 7) >> 1];
+                if (wh) {
+                    if (xh) mix_mac<1, 1>(t[r][m], cp, xp);
+                    else mix_mac<1, 0>(t[r][m], cp, xp);
+                } else {
+                    if (xh) mix_mac<0, 1>(t[r][m], cp, xp);
+                    else mix_mac<0, 0>(t[r][m], cp, xp);
+                }
+            }
+        if (k % 8 == 0) dep = t[0][0];
+        if (k % 8 == 7) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < MC; ++m) asm volatile("" : "+v"(t[r][m]));
+        }
+    }
+}
+
 template <int F, int R, int MC>
 __device__ __forceinline__ void segment_sums_rows(const u4_t (&w)[R], const DecodeConsts &kc,
                                                   const uint16_t *xs, int xo, int K,
                                                   float (&t)[R][MC]) {
+    if constexpr (F == FMT_TERN) {
+        tern_sums_rows<R, MC>(w, kc, xs, xo, K, t);
+        return;
+    }
     constexpr int STEPS = SegCodes<F>::v / 8;
     // `dep` carries a value of the previous step into the opaque offset, so
     // a step's reads can be issued once the previous step has started but

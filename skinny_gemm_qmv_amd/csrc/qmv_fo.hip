@@ -1203,16 +1203,13 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
         const size_t lds = (size_t)klen * 2 + lut;
         hipLaunchKernelGGL(k, dim3(gx(k, lds, D * QMV_ROWS1, stream_per_cu<NI, 1>()), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
                            a.N, a.K, seg_split, a.part);
-    } else if (F != FMT_TERN && wide_fits(klen, 1, mc_wide<NI>())) {
-        // (ternary has no several-column inner step: one activation row per workgroup)
-        if constexpr (F != FMT_TERN) {
-            constexpr int MCW = mc_wide<NI>();
-            auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false>;
-            const size_t lds = (size_t)MCW * klen * 2;
-            const int gy = (a.M + MCW - 1) / MCW;
-            hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), gy, S), dim3(kBlock), lds, st, wq, a.sc,
-                               a.x, a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
-        }
+    } else if (wide_fits(klen, 1, mc_wide<NI>()) && !(F == FMT_TERN && QMV_TERN_LUT)) {
+        constexpr int MCW = mc_wide<NI>();
+        auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false>;
+        const size_t lds = (size_t)MCW * klen * 2;
+        const int gy = (a.M + MCW - 1) / MCW;
+        hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), gy, S), dim3(kBlock), lds, st, wq, a.sc,
+                           a.x, a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
     } else {
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
         const size_t lds = (size_t)klen * 2 + lut;

@@ -37,6 +37,8 @@ def reference(d):
     (3, 257, 2560),
     (1, 70, 16384),     # longest K (205 segments)
     (5, 130, 1000),
+    (16, 300, 4096),    # four-row chunks
+    (7, 100, 16384),    # ragged chunk at the longest K (two-row chunks)
 ])
 def test_ternary_bit_exact(M, N, K):
     d = synth.ternary_inputs(M, N, K, salt=N + K)
