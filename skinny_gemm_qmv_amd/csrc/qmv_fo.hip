@@ -922,33 +922,44 @@ __device__ __forceinline__ void mxfp4_local(const uint16_t *stage, int rounds, i
 }
 
 // Fused activation-and-quantize ("Gemma 4 Optimization with Agentic Kernel
-// Engineering", "What it found"): after its units, a wave makes its fp16
-// outputs visible (release fence), then for every unit it produced and every
-// activation row adds one arrival to the unit's 32-row block.  The wave that
-// brings a block's count to 32 / (rows per unit) read all of it: it takes an
+// Engineering", "What it found"), for lane layouts whose workgroup rounds do
+// not cover whole 32-row blocks: the fp16 outputs go to the workspace; after
+// its units the workgroup makes them visible (each wave completes its
+// stores, a barrier, then one agent-scope release by wave 0), and wave 0
+// adds one arrival per unit of the workgroup to the unit's 32-row block.
+// The arrival that brings a block's count to 32 / (rows per unit) takes an
 // acquire fence, quantises the block from the staged fp16 values and resets
-// the counter to zero for the next call.  No wave waits for another.
+// the counter to zero for the next call.  No workgroup waits for another.
 template <int MC, class Eng>
 __device__ __forceinline__ void mxfp4_tail(const Eng &eng, const uint16_t *stage, uint8_t *qcodes,
                                            uint8_t *qscale, uint32_t *qcnt, int M, int N, int m0) {
     constexpr uint32_t kArrivals = 32 / Eng::kRowsPerUnit;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nblk = N / 32;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (wave != 0) return;  // no barrier follows
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    for (int u = eng.first; u < eng.total_units; u += eng.stride) {
-        const int blk = u * Eng::kRowsPerUnit / 32;
-#pragma unroll
-        for (int m = 0; m < MC; ++m) {
-            if (m0 + m >= M) break;  // uniform
+    // wave 0's units are the first of each round of the workgroup's kWaves
+    // consecutive units; lane t < kWaves * MC adds the arrival of unit
+    // u0 + t / MC, activation row t % MC (all in flight at once)
+    for (int u0 = eng.first; u0 < eng.total_units; u0 += eng.stride) {
+        const int tw = lane / MC, tm = lane % MC;
+        const int tu = u0 + tw;
+        const bool valid = lane < kWaves * MC && tu < eng.total_units && m0 + tm < M;
+        uint32_t old = 0;
+        if (valid)
+            old = __hip_atomic_fetch_add(&qcnt[(size_t)(m0 + tm) * nblk + tu * Eng::kRowsPerUnit / 32], 1u,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t last = __ballot(valid && old == kArrivals - 1);
+        while (last != 0) {  // uniform
+            const int t = __builtin_ctzll(last);
+            last &= last - 1;
+            const int m = t % MC, blk = (u0 + t / MC) * Eng::kRowsPerUnit / 32;
             const size_t c = (size_t)(m0 + m) * nblk + blk;
-            uint32_t old = 0;
-            if (lane == 0) old = __hip_atomic_fetch_add(&qcnt[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            old = __builtin_amdgcn_readfirstlane(old);
-            if (old != kArrivals - 1) continue;  // uniform
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             const uint16_t h = lane < 32 ? stage[(size_t)(m0 + m) * N + (size_t)blk * 32 + lane] : (uint16_t)0;
-            mx_quant_half(h, lane < 32, qcodes + (size_t)(m0 + m) * (N / 2) + (size_t)blk * 16,
-                          qscale + c);
+            mx_quant_half(h, lane < 32, qcodes + (size_t)(m0 + m) * (N / 2) + (size_t)blk * 16, qscale + c);
             if (lane == 0) __hip_atomic_store(&qcnt[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -1308,9 +1319,11 @@ static hipError_t gu_shape(const GateUpArgs &a, hipStream_t st) {
 hipError_t launch_fo_gateup(const GateUpArgs &a, hipStream_t st) {
     LaneShape sh;
     const int nseg = a.K / 64;
-    if (a.qcodes != nullptr && nseg <= 24) {
+    if (a.qcodes != nullptr && nseg <= 64) {
         // quantised output: eight lanes per row (eight rows per wave and unit),
-        // so that a workgroup's round covers whole 32-row blocks
+        // so that a workgroup's round covers whole 32-row blocks (longer rows
+        // use the counter fallback of mxfp4_tail)
+        if (nseg > 24) return gu_shape<8, 8, 8>(a, st);
         sh = nseg <= 8 ? LaneShape{8, 1, 1} : LaneShape{8, 3, 4};
     } else if (!pick_shape_rows(nseg, a.N, sh)) {
         return hipErrorInvalidValue;

@@ -39,6 +39,9 @@ def oargs(d):
     (1, 32, 1536),     # one block
     (4, 320, 1536),    # several rows per workgroup
     (9, 160, 2048),
+    (1, 1024, 4096),   # 64 segments per row: eight lanes x eight segments
+    (1, 96, 8192),     # 128 segments: the counter fallback
+    (3, 64, 6144),
 ])
 def test_gateup_mxfp4_bit_exact(M, N, K):
     d = synth.fused_inputs(M, N, K, salt=N + K)
