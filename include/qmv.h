@@ -175,8 +175,8 @@ qmv_status qmm_mxfp4(const uint8_t *wq, const uint8_t *e8m0, const uint16_t *x, 
  * codes k < K); the fp16 row scale multiplies the reduced total.
  *  wq uint8 [N][ceil(K/80)*16] (16-byte aligned); scale fp16 [N];
  *  x fp16 [M][K] (16-byte aligned); y as for qmv_int2.  K a multiple of 8,
- *  K <= 16384.  Several activation rows run one workgroup row each (every row
- *  streams the weights).  Mode: FIXED; no workspace. */
+ *  K <= 16384.  Several activation rows are taken in chunks that share each
+ *  weight read.  Mode: FIXED; no workspace. */
 qmv_status qmv_ternary(const uint8_t *wq, const uint16_t *scale, const uint16_t *x, void *y,
                        qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
                        size_t ws_bytes, void *stream);

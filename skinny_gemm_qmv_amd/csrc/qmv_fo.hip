@@ -53,9 +53,9 @@ bool pick_shape(int nseg, LaneShape &s) {
     return true;
 }
 
-// Few rows: when N fills fewer than ~4 row groups per SIMD, spread a row
-// over more lanes (fewer rows per wave, more waves) as long as at least half
-// of the row's lanes hold a segment.  The order of the sums does not depend
+// Few rows: when N fills fewer than one row group per SIMD (1024 on
+// MI355X), spread a row over more lanes (fewer rows per wave, more waves) as
+// long as at least half of the row's lanes hold a segment.  The order of the sums does not depend
 // on the layout.
 // Measured: the fused gate/up at N=8192 (1024 row groups of eight rows)
 // runs 7.7 us widened to 32 lanes per row and 6.0 us as is; the int2 matvec
