@@ -300,6 +300,7 @@ def sweep_cases():
         ("fused rmsnorm+int2 gate/up+gelu+mxfp4 quantise N=2x8192 K=1536 M=1", fused_quant_f4),
         ("fused rmsnorm+int2 q/k/v N=2048+512+512 K=1536 M=1", qkv_f1),
         ("mxfp4 expert gather E=32 top-4 N=5760 K=2880 M=1", gather_f2(1)),
+        ("mxfp4 expert gather E=32 top-4 N=5760 K=2880 M=16", gather_f2(16)),
         ("ternary N=16384 K=4096 M=1", ternary_m(1)),
         ("int2 lm_head+argmax N=262144 K=1536 M=1", argmax_c4(1)),
         ("int2 lm_head+argmax N=262144 K=1536 M=4", argmax_c4(4)),

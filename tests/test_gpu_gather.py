@@ -4,9 +4,9 @@ bit for bit.
 Each output plane y[m][j] is the fixed-order MXFP4 matvec of activation row m
 with expert idx[m][j], read in place from the [E][N][K/2] expert array.  The
 cases cover the gpt-oss-sized decode shape, ragged N, one segment per row,
-the longest K, many planes, duplicate ids in a row and across rows, the three
-output dtypes, and ids outside [0, E) (their plane is NaN, the others are
-untouched by it)."""
+the longest K, many planes (up to 132 over 32 experts), duplicate ids in a
+row and across rows, the three output dtypes, and ids outside
+[0, E) (their plane is NaN, the others are untouched by it)."""
 import numpy as np
 import pytest
 import torch
@@ -35,6 +35,9 @@ def run(d, idx=None, y_dtype=torch.float32):
     (1, 3, 3, 1000, 16384),   # longest K
     (16, 16, 4, 200, 512),    # 64 planes
     (4, 2, 2, 129, 2880),     # more picks than experts: every expert used twice
+    (64, 8, 2, 96, 256),      # ~16 planes per expert
+    (33, 32, 4, 640, 2880),   # 132 planes over 32 experts
+    (9, 5, 3, 70, 6144),      # long K, several planes per expert
 ])
 def test_gather_bit_exact(M, E, topk, N, K):
     d = synth.expert_inputs(M, E, topk, N, K, salt=N + K)
