@@ -392,6 +392,13 @@ def main():
 
     extra = []
     if not args.no_extra:
+        # the headline call hot: one weight copy, re-read from the caches
+        mk, nb, _, _ = int4_case(1, cold=False)
+        s = run_case(mk, max(20, args.steps // 10), max(5, args.warmup // 10))
+        extra.append({"workload": "int4 N=16384 K=4096 M=1 hot (one weight copy, cache-resident)",
+                      "us_per_call": round(s * 1e6, 3), "GB/s": round(effective_gbps(nb, s), 1),
+                      "bound": "hbm", "roofline_frac": round(roof_fraction("hbm", nb, 0, s), 4)})
+        del mk
         for label, b in sweep_cases():
             mk, nb, fl, bound = b()
             s = run_case(mk, max(20, args.steps // 10), max(5, args.warmup // 10))
