@@ -754,12 +754,7 @@ __device__ void rmsnorm_prologue(const uint16_t *__restrict__ x, const uint16_t 
 }
 
 // The same prologue for one activation row per workgroup (M = 1 decode),
-// shortened to one global round trip and one barrier before normalising:
-// every thread loads its gamma vectors at once; lane j of wave 0 loads the
-// x and residual values of segments j, j+64, ... itself, forms h, writes it
-// to LDS (and residual_out) and sums the squares from registers in the
-// fixed order; the tree and inv follow in the same wave.
-// One activation row (M = 1), in two phases so that the global loads of x,
+// in two phases so that the global loads of x,
 // the residual and gamma are issued before the weight prefetch (vector loads
 // retire in issue order: loaded after the weights, the prologue would wait
 // for them).  load(): every thread takes one 16-byte vector of x, r and
