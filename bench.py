@@ -397,6 +397,7 @@ def main():
         s = run_case(mk, max(20, args.steps // 10), max(5, args.warmup // 10))
         extra.append({"workload": "int4 N=16384 K=4096 M=1 hot (one weight copy, cache-resident)",
                       "us_per_call": round(s * 1e6, 3), "GB/s": round(effective_gbps(nb, s), 1),
+                      "TFLOP/s": round(2 * 16384 * 4096 / s / 1e12, 3),
                       "bound": "hbm", "roofline_frac": round(roof_fraction("hbm", nb, 0, s), 4)})
         del mk
         for label, b in sweep_cases():
