@@ -144,16 +144,25 @@ constexpr int ring_depth() {
 }
 
 // Rows blocked per unit: several activation columns read from LDS use each
-// activation value for QMV_ROWS rows; one column keeps the register copy.
+// activation value for QMV_ROWS rows (QMV_ROWS_MX for MXFP4, whose bf16
+// activations take one widening instruction per value and column); one
+// column keeps the register copy.  Measured on MI355X (N=21504, K=5376,
+// bit-identical results): MXFP4 M = 16 / 64 / 256 take 120.5 / 441.9 /
+// 1761.5 us with two rows, 112.5 / 406.3 / 1569.4 with four, 125.1 / 460.2 /
+// 1797.4 with eight; int4 (N=16384, K=4096) M = 4 takes 20.9 us with two
+// rows and 25.9 with four, M = 8 and 16 within 3 %.
 #ifndef QMV_ROWS
 #define QMV_ROWS 2
 #endif
 #ifndef QMV_ROWS1
 #define QMV_ROWS1 1
 #endif
-template <int MC, bool XREG>
+#ifndef QMV_ROWS_MX
+#define QMV_ROWS_MX 4
+#endif
+template <int MC, bool XREG, int F = -1>
 constexpr int rows_block() {
-    return (MC > 1 && !XREG) ? QMV_ROWS : (MC == 1 ? QMV_ROWS1 : 1);
+    return (MC > 1 && !XREG) ? (F == FMT_MXFP4 ? QMV_ROWS_MX : QMV_ROWS) : (MC == 1 ? QMV_ROWS1 : 1);
 }
 
 // Raw loaded bits only: converting a scale in the load routine would make
@@ -652,7 +661,7 @@ __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict_
     const uint16_t *xz = x + (size_t)seg0 * CODES;
     const uint8_t *const w1[1] = {wq};
     const void *const s1[1] = {sc};
-    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG>()> eng(w1, s1, N, klen, seg0,
+    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG, F>()> eng(w1, s1, N, klen, seg0,
                                                                                        nseg_row);
     XStage<MC> xst;
     xst.load(xz, M, K, klen, m0, kval);
