@@ -1,0 +1,48 @@
+"""Host logic of the benchmark (no GPU): the one-GPU guard, the roofline
+fractions and the digest check that decides whether stored HBM counter
+readings still describe the kernels being timed."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_effective_bandwidth_and_roofline_fractions():
+    # 8 GB moved in one second is exactly the HBM peak
+    assert bench.effective_gbps(8e9, 1.0) == pytest.approx(8.0)
+    assert bench.roof_fraction("hbm", 4e9, 0, 1.0) == pytest.approx(4.0 / bench.HBM_PEAK_GBS)
+    # half the dense bf16 matrix-core rate
+    assert bench.roof_fraction("mfma", 0, bench.BF16_MFMA_PEAK / 2, 1.0) == pytest.approx(0.5)
+    # fixed-order arithmetic counts one FMA (two flops) per code and column
+    fl = 2 * bench.FP32_VALU_FMA_PER_S * 0.25
+    assert bench.roof_fraction("alu", 0, fl, 1.0) == pytest.approx(0.25)
+
+
+def test_source_digest_is_stable_and_hex():
+    a, b = bench.source_digest(), bench.source_digest()
+    assert a == b and len(a) == 16 and int(a, 16) >= 0
+
+
+def test_stored_traffic_follows_the_digest(tmp_path, monkeypatch):
+    rec = {"source_digest": "0123456789abcdef", "hbm_bytes_per_launch": 12345}
+    (tmp_path / "t.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.stored_traffic("t.json", "0123456789abcdef") == 12345
+    assert bench.stored_traffic("t.json", "fedcba9876543210") is None
+    assert bench.stored_traffic("missing.json", "0123456789abcdef") is None
+
