@@ -195,8 +195,9 @@ qmv_status qmv_ternary(const uint8_t *wq, const uint16_t *scale, const uint16_t 
  *         exponent clamped to [-87, 87], exp by the library's own
  *         Cody-Waite + degree-7 polynomial.
  *  x, residual fp16 [M][K] (16-byte aligned); residual_out fp16 [M][K] or NULL
- *  (receives h); gamma fp16 [K]; wq_* uint32 [N][K/16]; s_* fp16 [N];
- *  out fp16 [M][N].  K a multiple of 64, K <= 16384.  Mode: FIXED. */
+ *  (receives h; 16-byte aligned); gamma fp16 [K] (16-byte aligned);
+ *  wq_* uint32 [N][K/16] (16-byte aligned); s_* fp16 [N]; out fp16 [M][N].
+ *  K a multiple of 64, K <= 16384.  Mode: FIXED. */
 qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *residual,
                                         uint16_t *residual_out, const uint16_t *gamma, float eps,
                                         const uint32_t *wq_gate, const uint16_t *s_gate,
@@ -214,7 +215,7 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *resid
  * the nearest E2M1 value, ties to the even code, clamped to +-6, sign kept;
  * element 2j in the low nibble of byte j, 2j+1 in the high nibble (the
  * layout qmm_mxfp4 reads).
- *  Inputs as for qmv_int2_rmsnorm_gateup_gelu; codes uint8 [M][N/2], e8m0
+ *  Inputs (and their alignment) as for qmv_int2_rmsnorm_gateup_gelu; codes uint8 [M][N/2], e8m0
  *  uint8 [M][N/32]; N a multiple of 32.  Needs a workspace of
  *  qmv_workspace_size(QMV_OP_INT2_GATEUP_MXFP4, M, N, K, FIXED) bytes
  *  (256-byte aligned: per-block arrival counters and fp16 staging), zeroed
@@ -240,8 +241,8 @@ qmv_status qmv_quant_mxfp4(const uint16_t *v, uint8_t *codes, uint8_t *e8m0, int
  *   y_q = int2 matvec (wq_q, s_q), y_k = (wq_k, s_k), y_v = (wq_v, s_v),
  * each exactly as qmv_int2 would compute it from xn (bit-exact).
  *  x, residual fp16 [M][K] (16-byte aligned); residual_out fp16 [M][K] or
- *  NULL (receives h); gamma fp16 [K]; wq_z uint32 [N_z][K/16] (16-byte
- *  aligned); s_z fp16 [N_z]; y_z [M][N_z] in y_dtype (fp32 default, or one
+ *  NULL (receives h; 16-byte aligned); gamma fp16 [K] (16-byte aligned);
+ *  wq_z uint32 [N_z][K/16] (16-byte aligned); s_z fp16 [N_z]; y_z [M][N_z] in y_dtype (fp32 default, or one
  *  RNE rounding to fp16 / bf16), each N_z >= 1 and M*N_z*4 bytes < 4 GiB.
  *  K a multiple of 64, K <= 16384.  Mode: FIXED; no workspace. */
 qmv_status qmv_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uint16_t *residual_out,

@@ -129,13 +129,19 @@ def workspace_init(ws, stream=None):
            "qmv_workspace_init")
 
 
-def _workspace(op, M, N, K, mode, workspace):
+def _workspace(op, M, N, K, mode, workspace, stream):
+    """The caller's workspace, or a temporary one allocated and zeroed on the
+    stream the kernel runs on: the zero-fill is then ordered before the
+    kernel, and the caching allocator hands the block to later work on that
+    stream only, which runs after the kernel."""
     need = workspace_size(op, M, N, K, mode)
     if workspace is None:
         if need == 0:
             return None, 0
-        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
-        workspace_init(workspace)
+        s = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(s):
+            workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+            workspace_init(workspace, stream=s)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -149,7 +155,7 @@ def _matvec(fn, name, wq, sc, x, y, y_dtype, mode, workspace, stream, op):
     M, K = x.shape
     N = wq.shape[0]
     y = _out(y, M, N, y_dtype, x.device)
-    ws, wsb = _workspace(op, M, N, K, mode, workspace)
+    ws, wsb = _workspace(op, M, N, K, mode, workspace, stream)
     _check(fn(_ptr(wq), _ptr(sc), _ptr(x), _ptr(y), _DTYPES[y_dtype], M, N, K, _mode(mode),
               _ptr(ws), wsb, _stream(stream)), name)
     return y
@@ -200,7 +206,7 @@ def qmv_int2_rmsnorm_gateup_gelu(x, residual, gamma, eps, wq_gate, s_gate, wq_up
     out = _out(out, M, N, torch.float16, x.device)
     if residual_out is not None:
         _req(residual_out, "residual_out", torch.float16, (M, K))
-    ws, wsb = _workspace("int2_gateup", M, N, K, mode, workspace)
+    ws, wsb = _workspace("int2_gateup", M, N, K, mode, workspace, stream)
     _check(_lib.qmv_int2_rmsnorm_gateup_gelu(
         _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps), _ptr(wq_gate),
         _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(out), M, N, K, _mode(mode), _ptr(ws), wsb,
@@ -230,7 +236,7 @@ def qmv_int2_rmsnorm_gateup_gelu_mxfp4(x, residual, gamma, eps, wq_gate, s_gate,
         _req(e8m0, "e8m0", torch.uint8, (M, N // 32))
     if residual_out is not None:
         _req(residual_out, "residual_out", torch.float16, (M, K))
-    ws, wsb = _workspace("int2_gateup_mxfp4", M, N, K, mode, workspace)
+    ws, wsb = _workspace("int2_gateup_mxfp4", M, N, K, mode, workspace, stream)
     _check(_lib.qmv_int2_rmsnorm_gateup_gelu_mxfp4(
         _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(gamma), float(eps), _ptr(wq_gate),
         _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(codes), _ptr(e8m0), M, N, K, _mode(mode), _ptr(ws), wsb,
@@ -325,7 +331,7 @@ def qmv_int2_argmax(wq, scale, x, idx=None, maxval=None, logits=None, want_maxva
         maxval = torch.empty(M, dtype=torch.float32, device=dev)
     if logits is None and want_logits:
         logits = torch.empty((M, N), dtype=torch.float32, device=dev)
-    ws, wsb = _workspace("int2_argmax", M, N, K, mode, workspace)
+    ws, wsb = _workspace("int2_argmax", M, N, K, mode, workspace, stream)
     _check(_lib.qmv_int2_argmax(_ptr(wq), _ptr(scale), _ptr(x), _ptr(idx), _ptr(maxval),
                                 _ptr(logits), M, N, K, _mode(mode), _ptr(ws), wsb, _stream(stream)),
            "qmv_int2_argmax")

@@ -24,9 +24,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqmv.so")
+MEASURE_LIB = os.path.join(PKG, "libqmv_measure.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["qmv_api.hip", "qmv_fo.hip", "qmv_mfma.hip"]
+# the benchmark's reference kernels (streaming read, empty kernel): a library
+# of their own, so that the product library holds only the method
+MEASURE_SOURCES = ["qmv_measure.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -49,12 +53,12 @@ def _compile(src, build_dir=BUILD, defines=()):
     return obj, err
 
 
-def build(verbose=False, out=LIB, defines=(), build_dir=BUILD):
+def build(verbose=False, out=LIB, defines=(), build_dir=BUILD, sources=SOURCES):
     """Compile every HIP source for gfx950 and link libqmv.so; returns its path.
     `defines` (NAME=VALUE strings) and `out` build a variant elsewhere, e.g. to
     compare launch shapes (QMV_BLOCK, QMV_MAX_GRID, QMV_RING, QMV_XREG_BUDGET)."""
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=len(sources)) as ex:
+        results = list(ex.map(lambda src: _compile(src, build_dir, defines), sources))
     for _, err in results:
         if err.strip() and verbose:
             sys.stderr.write(err + "\n")
@@ -68,5 +72,11 @@ def build(verbose=False, out=LIB, defines=(), build_dir=BUILD):
     return out
 
 
+def build_measure(verbose=False):
+    """Compile the benchmark's reference kernels into libqmv_measure.so."""
+    return build(verbose=verbose, out=MEASURE_LIB, sources=MEASURE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_measure(verbose=True))

@@ -182,8 +182,9 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu(const uint16_t *x, const uint16_t *resid
     if (!fits_32bit(N, K, 4)) return QMV_ERR_UNSUPPORTED;
     // out (fp16 [M][N]) is written with 32-bit byte offsets
     if ((uint64_t)M * (uint64_t)N * 2u >= (1ull << 32) - (1ull << 16)) return QMV_ERR_UNSUPPORTED;
+    // the prologue reads gamma and writes residual_out as 16-byte vectors
     if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(wq_gate, 16) || !aligned(wq_up, 16) ||
-        !aligned(gamma, 2) || !aligned(out, 2) || (residual_out && !aligned(residual_out, 2)))
+        !aligned(gamma, 16) || !aligned(out, 2) || (residual_out && !aligned(residual_out, 16)))
         return QMV_ERR_ALIGNMENT;
     if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
     qmv::GateUpArgs a{x, residual, gamma, residual_out, eps, wq_gate, wq_up, s_gate, s_up, out, M, N, K};
@@ -203,7 +204,7 @@ qmv_status qmv_int2_rmsnorm_gateup_gelu_mxfp4(const uint16_t *x, const uint16_t 
     if (!fits_32bit(N, K, 4)) return QMV_ERR_UNSUPPORTED;
     if ((uint64_t)M * (uint64_t)N * 2u >= (1ull << 32) - (1ull << 16)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(wq_gate, 16) || !aligned(wq_up, 16) ||
-        !aligned(gamma, 2) || (residual_out && !aligned(residual_out, 2)))
+        !aligned(gamma, 16) || (residual_out && !aligned(residual_out, 16)))
         return QMV_ERR_ALIGNMENT;
     if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
     const size_t need = qmv::gateup_mxfp4_workspace_bytes(M, N);
@@ -248,8 +249,8 @@ qmv_status qmv_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uin
     if ((uint64_t)Nq + Nk + Nv > 0x7FFFFFFFull) return QMV_ERR_UNSUPPORTED;
     const size_t es = dtype_size(y_dtype);
     if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(wq_q, 16) || !aligned(wq_k, 16) ||
-        !aligned(wq_v, 16) || !aligned(gamma, 2) || !aligned(y_q, es) || !aligned(y_k, es) || !aligned(y_v, es) ||
-        (residual_out && !aligned(residual_out, 2)))
+        !aligned(wq_v, 16) || !aligned(gamma, 16) || !aligned(y_q, es) || !aligned(y_k, es) || !aligned(y_v, es) ||
+        (residual_out && !aligned(residual_out, 16)))
         return QMV_ERR_ALIGNMENT;
     if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
     qmv::QkvArgs a{x, residual, gamma, residual_out, eps, {wq_q, wq_k, wq_v}, {s_q, s_k, s_v},

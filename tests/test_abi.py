@@ -100,6 +100,11 @@ def test_gateup_validation():
     assert call(a) == INVALID
     a = list(args); a[0] = P(18)
     assert call(a) == ALIGN
+    # the prologue reads gamma and writes residual_out as 16-byte vectors
+    a = list(args); a[3] = P(18)
+    assert call(a) == ALIGN
+    a = list(args); a[2] = P(34)
+    assert call(a) == ALIGN
     assert call(args, mode=2) == UNSUP    # matrix-core mode never applies to int2
     assert call(args, M=256, N=1 << 23) == UNSUP  # fp16 output of M*N*2 >= 4 GiB (32-bit offsets)
 
@@ -123,6 +128,8 @@ def test_qkv_validation():
     assert call(eps=-1.0) == INVALID
     assert call({6: 24}) == ALIGN
     assert call({10: 18}) == ALIGN
+    assert call({3: 18}) == ALIGN          # gamma: 16-byte vectors
+    assert call({2: 40}) == ALIGN          # residual_out: 16-byte vectors
     assert call(mode=1) == UNSUP
     assert call(M=256, Ns=(64, 1 << 22, 64)) == UNSUP  # y_k of M*N*4 >= 4 GiB
 
@@ -176,6 +183,8 @@ def test_gateup_mxfp4_validation():
     assert call(K=96) == INVALID
     assert call(eps=-1.0) == INVALID
     assert call({4: 24}) == ALIGN
+    assert call({3: 18}) == ALIGN          # gamma: 16-byte vectors
+    assert call({2: 40}) == ALIGN          # residual_out: 16-byte vectors
     assert call(mode=1) == UNSUP
     assert call() == WS                    # workspace required
     need = q._lib.qmv_workspace_size(8, 1, 64, 64, 0)
@@ -235,3 +244,30 @@ def test_splitk_workspace_size_and_validation():
     assert _mv(fn, M=1, N=2048, K=1536, mode=1) == WS
     assert _mv(fn, M=1, N=2048, K=1536, mode=1, ws=4096, wsb=need - 4) == WS
     assert _mv(fn, M=1, N=2048, K=1536, mode=1, ws=4096 + 16, wsb=need) == ALIGN
+
+
+MEASURE_HEADER = os.path.join(ROOT, "include", "qmv_measure.h")
+MEASURE_LIB = os.path.join(ROOT, "skinny_gemm_qmv_amd", "libqmv_measure.so")
+
+
+def test_measure_library_exports_its_header():
+    """The benchmark's reference kernels (streaming read, empty kernel): every
+    function include/qmv_measure.h declares is exported, and the streaming
+    read rejects bad arguments before touching the GPU."""
+    if not os.path.exists(MEASURE_LIB):
+        pytest.skip("libqmv_measure.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(MEASURE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(qmv_measure_\w+)\s*\(", text)))
+    assert names == ["qmv_measure_empty", "qmv_measure_stream_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", MEASURE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, flags=re.M))
+    assert all(n in exported for n in names)
+    lib = C.CDLL(MEASURE_LIB)
+    fn = lib.qmv_measure_stream_read
+    fn.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    assert fn(None, 4096, P(256), 0, None) == 1
+    assert fn(P(256), 4096, None, 0, None) == 1
+    assert fn(P(256), 0, P(256), 0, None) == 1
+    assert fn(P(256), 4100, P(256), 0, None) == 1      # not a multiple of 16 bytes
+    assert fn(P(264), 4096, P(256), 0, None) == 1      # source not 16-byte aligned

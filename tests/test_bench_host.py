@@ -46,3 +46,36 @@ def test_stored_traffic_follows_the_digest(tmp_path, monkeypatch):
     assert bench.stored_traffic("t.json", "fedcba9876543210") is None
     assert bench.stored_traffic("missing.json", "0123456789abcdef") is None
 
+
+
+def test_headline_bytes_are_the_lm_head_stream():
+    # packed int2 weights (K/4 bytes a row), fp16 row scales, fp16
+    # activations, and the index + maximum written per activation row
+    assert bench.argmax_bytes(1) == 262144 * 1536 // 4 + 262144 * 2 + 1536 * 2 + 8 == 101_190_664
+    assert bench.argmax_bytes(4) - bench.argmax_bytes(1) == 3 * (1536 * 2 + 8)
+
+
+def test_gather_counts_each_distinct_expert_once():
+    import numpy as np
+    E, N, K = 32, 5760, 2880
+    eb = N * K // 2 + N * (K // 32)
+    ids = np.array([[0, 1, 2, 3], [3, 2, 1, 0]], np.int32)  # two rows, the same four experts
+    assert bench.gather_bytes(ids, E, N, K, 2, 4) == 4 * eb + 2 * K * 2 + 2 * 4 * 4 + 2 * 4 * N * 4
+    ids2 = np.array([[0, 1, 2, 3], [4, 5, 6, 7]], np.int32)
+    assert bench.gather_bytes(ids2, E, N, K, 2, 4) - bench.gather_bytes(ids, E, N, K, 2, 4) == 4 * eb
+    # an id outside [0, E) reads no expert
+    assert bench.gather_bytes(np.array([[0, 40]], np.int32), E, N, K, 1, 2) == eb + K * 2 + 2 * 4 + 2 * N * 4
+
+
+def test_timed_rotation_continues_after_the_warmup(monkeypatch):
+    seen = []
+    monkeypatch.setattr(bench, "graph_of", lambda calls: [c() for c in calls] and calls)
+    monkeypatch.setattr(bench, "time_graph", lambda g: 1.0)
+    sec = bench.run_case(lambda i: (lambda: seen.append(i)), steps=7, warmup=3)
+    assert seen == list(range(10))   # warmup 0..2, timed 3..9: no copy is re-read back to back
+    assert sec == 1.0 / 7
+
+
+def test_default_run_is_bounded():
+    a = bench.parse([])
+    assert a.gpus == 1 and a.steps * 37e-6 < 60 and a.warmup < a.steps
