@@ -147,7 +147,12 @@ qmv_status qmv_int2(const uint32_t *wq, const uint16_t *scale, const uint16_t *x
                     qmv_dtype y_dtype, int M, int N, int K, qmv_mode mode, void *workspace,
                     size_t ws_bytes, void *stream);
 
-/* int4 symmetric (value q-8) with fp16 scales per 32-element group.
+/* int4 symmetric (value q-8) with fp16 scales per 32-element group: the
+ * 4-bit quantized matvec ("26 Iterations: Porting Cleanroom Kernels to
+ * Gemma 4", "The Dead Ends": the 4-bit Q4K kernel; "raw-Metal loop
+ * playbook", next-target table: QAT-int4 weights), dequantized inside the
+ * dot product ("26 Iterations", "The Wins": scalar inline-dequant), in the
+ * fixed order above with one group scale per 16-byte segment.
  *  wq uint32 [N][K/8] (16-byte aligned); scales fp16 [N][K/32]; x fp16 [M][K]
  *  (16-byte aligned); y as for qmv_int2.  K a multiple of 32, K <= 16384.
  *  Modes: FIXED, SPLITK. */

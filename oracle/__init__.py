@@ -63,6 +63,7 @@ def _bind(lib):
         "orc_qmm_mxfp4": ([vp, vp, vp, vp, i64, i64, i64, i32], None),
         "orc_exp": ([f32], f32),
         "orc_gelu": ([f32], f32),
+        "orc_probe_mul_add": ([f32, f32, f32], f32),
         "orc_rmsnorm_prologue": ([vp, vp, vp, f32, i64, vp, vp], f32),
         "orc_int2_rmsnorm_gateup_gelu": ([vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp,
                                           i64, i64, i64, i32], None),

@@ -575,6 +575,18 @@ ORC_API float orc_exp(float z)
     return p * two_n;
 }
 
+/* Build guard (no part of the method): a * b + c with the product and the
+ * sum rounded separately, written as every unfused step of this file is.  A
+ * build that contracts it into one fused multiply-add (for example
+ * -ffp-contract=fast with FMA instructions available) rounds once instead;
+ * the pins call it where the two differ, so such a build is rejected even
+ * where no method output happens to change. */
+ORC_API float orc_probe_mul_add(float a, float b, float c)
+{
+    float p = a * b;
+    return p + c;
+}
+
 #define ORC_SQRT_2_OVER_PI 0x1.988454p-1f
 #define ORC_GELU_C 0x1.6e4e26p-5f /* 0.044715 */
 

@@ -1,7 +1,8 @@
 // qmv_api.hip -- the extern "C" entry points declared in include/qmv.h:
 // argument validation, mode checks, workspace sizing and kernel dispatch.
 // No allocation, no host synchronisation, no global mutable state apart
-// from the per-thread text of the last HIP error.
+// from the per-thread text of the last HIP error and the per-device
+// launch-shape caches of qmv_internal.hpp (idempotent values).
 #include <stdio.h>
 #include <string.h>
 

@@ -46,6 +46,21 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return u2f((uint32_t)b << 16); }
 
+// Compile-time loop: f(Index<0>{}) ... f(Index<N-1>{}), always expanded
+// (a #pragma unroll may be refused for a large body).
+template <int I> struct Index { static constexpr int value = I; };
+template <int I, int N, class Fn>
+__device__ __forceinline__ void static_for_from(Fn &&f) {
+    if constexpr (I < N) {
+        f(Index<I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn &&f) {
+    static_for_from<0, N>(f);
+}
+
 __device__ __forceinline__ h2_t fma_h2(h2_t a, float mul, float add) {
     const h2_t m = {(_Float16)mul, (_Float16)mul};
     const h2_t c = {(_Float16)add, (_Float16)add};
@@ -74,7 +89,6 @@ struct DecodeConsts {
     uint32_t m2[5];                // int2 field masks, fields i and i+8 at bits 2i / 2i+16
     uint32_t m4lo, m4hi, xor2;     // int4 masks, int2 bias flip
     uint32_t m8;                   // ternary byte-pair mask
-    const uint8_t *lut = nullptr;  // ternary byte table in LDS (this lane's copy), or null
     __device__ __forceinline__ DecodeConsts() {
         magic = in_vgpr(kMagic1024);
         m2[0] = in_sgpr(0x00030003u);
@@ -176,93 +190,12 @@ __device__ __forceinline__ void mix_mac(float &acc, uint32_t a2, uint32_t b2) {
         asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "+v"(acc) : "v"(a2), "v"(b2));
 }
 
-// Decode through the LDS byte table (the pages' lookup-table decode) instead
-// of arithmetic.  Off by default: measured on MI355X at N=16384 (one
-// activation row) the table is no faster at K=4096 (11.2 vs 11.4 us) and
-// slower at K=2560 (7.7-9.0 vs 7.0 us) and with four rows (42-46 vs 35 us).
-// A wave's 64 lanes read random entries, and dword j of every 16-byte entry
-// falls in one of only eight banks, so the reads conflict; the table also
-// takes 16-32 KB of LDS per workgroup.  Both decodes give identical bits.
-#ifndef QMV_TERN_LUT
-#define QMV_TERN_LUT 0
-#endif
-
-// Ternary byte table in LDS: entry b holds the five values t_i - 1 of byte b
-// as fp16 (dwords: (v0, v1), (v2, v3), (v4, 0), 16 bytes with padding), in
-// kTernCopies interleaved copies: copy r of entry b sits at (b * copies + r)
-// * 16, so its three dwords fall in banks 4r .. 4r+2 whatever b is, and the
-// eight lanes that read together (one copy each) never share a bank.
-#ifndef QMV_TERN_COPIES
-#define QMV_TERN_COPIES 8
-#endif
-constexpr int kTernCopies = QMV_TERN_COPIES;
-constexpr int kTernLutBytes = 256 * kTernCopies * 16;
-
-// Fill the table (every thread of the workgroup takes part; a barrier must
-// follow).  Digit i of b is floor(b / 3^i) mod 3 for every byte value.
-__device__ __forceinline__ void tern_fill_lut(uint8_t *lut) {
-    for (int b = threadIdx.x; b < 256; b += blockDim.x) {
-        uint32_t h[6] = {0u, 0u, 0u, 0u, 0u, 0u};
-        uint32_t d = (uint32_t)b;
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const uint32_t t = d % 3u;
-            d /= 3u;
-            h[i] = t == 0u ? 0xBC00u : (t == 1u ? 0x0000u : 0x3C00u);  // -1, 0, +1
-        }
-        const u4_t e = {h[0] | h[1] << 16, h[2] | h[3] << 16, h[4], 0u};
-#pragma unroll
-        for (int r = 0; r < kTernCopies; ++r)
-            *reinterpret_cast<u4_t *>(lut + (size_t)(b * kTernCopies + r) * 16) = e;
-    }
-}
-
 // Ternary inner step (80 codes per segment): for k = 0 .. 79 in order,
 // t[a][m] = t[a][m] (+) value_k * x[m][k]; the words are decoded as the
 // codes reach them and each 16-byte activation vector is fetched once.
 template <int NS, int MC, class XF>
 __device__ __forceinline__ void tern_sums(const u4_t (&w)[NS], const DecodeConsts &kc, XF &&xf,
                                           float (&t)[NS][MC]) {
-#if QMV_TERN_LUT
-    // table decode: one 12-byte LDS read per byte gives its five values; the
-    // segment's 16 reads are all issued before the first product, so their
-    // latency overlaps the chain instead of stalling it byte by byte
-    u3_t ent[NS][16];
-    u4_t xa[NS][MC];
-#pragma unroll
-    for (int a = 0; a < NS; ++a)
-#pragma unroll
-        for (int y = 0; y < 16; ++y) {
-            const uint32_t b = (w[a][y / 4] >> (8 * (y % 4))) & 0xFFu;
-            ent[a][y] = *reinterpret_cast<const u3_t *>(kc.lut + (b << 4) * kTernCopies);
-        }
-#pragma unroll
-    for (int k = 0; k < 80; ++k) {
-        if (k % 8 == 0) {
-#pragma unroll
-            for (int a = 0; a < NS; ++a)
-#pragma unroll
-                for (int m = 0; m < MC; ++m) xa[a][m] = xf(a, m, k / 8);
-        }
-        const int dig = k % 5;
-        const bool wh = dig & 1, xh = k & 1;
-#pragma unroll
-        for (int a = 0; a < NS; ++a) {
-            const uint32_t cp = ent[a][k / 5][dig >> 1];
-#pragma unroll
-            for (int m = 0; m < MC; ++m) {
-                const uint32_t xp = xa[a][m][(k & 7) >> 1];
-                if (wh) {
-                    if (xh) mix_mac<1, 1>(t[a][m], cp, xp);
-                    else mix_mac<1, 0>(t[a][m], cp, xp);
-                } else {
-                    if (xh) mix_mac<0, 1>(t[a][m], cp, xp);
-                    else mix_mac<0, 0>(t[a][m], cp, xp);
-                }
-            }
-        }
-    }
-#else
     h2_t c[NS][10];
     u4_t xa[NS][MC];
 #pragma unroll
@@ -296,7 +229,6 @@ __device__ __forceinline__ void tern_sums(const u4_t (&w)[NS], const DecodeConst
             }
         }
     }
-#endif
 }
 
 // Inner step for the NS segments a lane holds in one row group, for MC

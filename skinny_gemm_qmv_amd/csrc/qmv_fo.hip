@@ -202,7 +202,6 @@ struct FoEngine {
     static constexpr int kRowsPerUnit = R * RPG;
 
     int N, K, nseg, P2, q, rsub, total_units, stride, first;
-    const uint8_t *tern_lut = nullptr;  // ternary: this lane's copy of the LDS byte table
     uint32_t row_bytes, srow;
     // Buffer descriptors (SGPRs) for the packed weights and their scales.
     // Raw buffer loads take a 32-bit per-lane offset and return zero for any
@@ -397,7 +396,6 @@ struct FoEngine {
     template <class Epi>
     __device__ __forceinline__ void run_stream(const uint16_t *xs, Epi &epi) {
         DecodeConsts kc;
-        kc.lut = tern_lut;
         u4_t xr[XREG && !kXf32 ? NI : 1][XREG && !kXf32 ? XV : 1];
         float xw[kXf32 ? NI : 1][kXf32 ? CODES : 1];
         int xoff[NI];
@@ -501,7 +499,6 @@ struct FoEngine {
             return;
         }
         DecodeConsts kc;
-        kc.lut = tern_lut;
         // x slice of this lane: segments q + RL*i (zeros past the row end)
         u4_t xr[XREG ? NI : 1][XREG ? MC : 1][XREG ? XV : 1];
         if constexpr (XREG) {
@@ -551,8 +548,12 @@ struct FoEngine {
                         for (int i = 0; i < NI; ++i) asm volatile("" : "+v"(xoff[i]));
                     }
                     float tot[R][NMAT][MC];
-#pragma unroll
-                    for (int t = 0; t < NMAT; ++t) {
+                    // expanded at compile time: with two matrices and eight
+                    // segments per lane the body is past the unroller's size
+                    // limit, and a rolled loop would index register arrays
+                    // at run time (scratch memory)
+                    static_for<NMAT>([&](auto tc) {
+                        constexpr int t = decltype(tc)::value;
                         float acc[R][MC][NI];
                         if constexpr (R == 1 && MC == 1) {
                             // one row, one column: the lane's segments are the
@@ -576,8 +577,8 @@ struct FoEngine {
                             // rows x columns are the independent chains;
                             // segments go one after another so only one
                             // segment's codes and activations are live
-#pragma unroll
-                            for (int i = 0; i < NI; ++i) {
+                            static_for<NI>([&](auto ic) {
+                                constexpr int i = decltype(ic)::value;
                                 u4_t wr[R];
 #pragma unroll
                                 for (int r = 0; r < R; ++r) wr[r] = cur.w[t][r][i];
@@ -594,13 +595,13 @@ struct FoEngine {
                                 // keep the next segment's LDS reads from being
                                 // scheduled ahead of this one (register budget)
                                 __builtin_amdgcn_sched_barrier(0);
-                            }
+                            });
                         }
 #pragma unroll
                         for (int r = 0; r < R; ++r)
 #pragma unroll
                             for (int m = 0; m < MC; ++m) tot[r][t][m] = finish(acc[r][m], cur.seg[t][r]);
-                    }
+                    });
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         float rs[NMAT];
@@ -667,13 +668,6 @@ __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict_
     xst.load(xz, M, K, klen, m0, kval);
     eng.prefetch();
     xst.store(xz, xs, M, K, klen, m0, kval);
-    if constexpr (F == FMT_TERN && QMV_TERN_LUT) {
-        // the byte table follows the staged activations (klen * 2 bytes, a
-        // multiple of 160); each lane reads copy lane % kTernCopies
-        uint8_t *lut = reinterpret_cast<uint8_t *>(xs) + (size_t)MC * klen * 2;
-        tern_fill_lut(lut);
-        eng.tern_lut = lut + (threadIdx.x % kTernCopies) * 16;
-    }
     __syncthreads();
     StoreEpi<F, MC> epi{OutBuf(part == nullptr ? y : static_cast<void *>(part + (size_t)blockIdx.z * M * N),
                                (uint32_t)M * (uint32_t)N, part == nullptr ? y_dtype : 0),
@@ -1014,9 +1008,10 @@ __global__ __launch_bounds__(kBlock) void k_fo_gateup(
 // activation row into a 64-bit key in the workspace with an agent-scope
 // atomic max (order-independent, so the result is exact).  Only after those
 // atomics have returned does the workgroup take a ticket from the completion
-// counter; the workgroup that takes the last ticket reads each key with an
-// atomic exchange (which also resets it to zero), writes idx / maxval and
-// resets the counter, leaving the workspace zeroed for the next call.
+// counter; the workgroup that
+// takes the last ticket reads each key with an atomic exchange (which also
+// resets it to zero), writes idx / maxval and resets the counter, leaving the
+// workspace zeroed for the next call.
 template <int MC>
 struct ArgmaxEpi {
     float *logits;
@@ -1087,6 +1082,17 @@ __global__ __launch_bounds__(kBlock) void k_fo_argmax(const uint32_t *__restrict
     }
     __syncthreads();
     if (threadIdx.x == 0) {
+        // Relaxed on purpose.  The key updates and the final exchanges are
+        // agent-scope atomic read-modify-writes, performed at the device's
+        // coherence point in the order they reach it; a workgroup asks for
+        // its ticket only after its key updates have returned (their values
+        // are consumed before the barrier), and the last workgroup issues its
+        // exchanges only after its ticket has returned, so every update is
+        // performed before the exchange that reads it.  No ordinary store
+        // needs publishing.  (An acquire-release ticket would also give the
+        // language-level ordering, but at agent scope it writes back the
+        // XCD's L2 once per workgroup: measured 56 vs 36 us per call on the
+        // N=262144 lm_head.)
         const uint32_t ticket = __hip_atomic_fetch_add(&counter[blockIdx.y], 1u, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
         is_last = (ticket == gridDim.x - 1) ? 1 : 0;
@@ -1127,11 +1133,8 @@ static int grid_for(Kern kernel, size_t lds, long N, int RL, int depth, int per_
     const int rpg = 64 / RL;
     const long total_rg = ((long)N + rpg - 1) / rpg;
     long g = (total_rg + (long)kWaves * depth - 1) / ((long)kWaves * depth);
-    int dev = 0, cus = 256, occ = 1;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kBlock, lds) != hipSuccess || occ < 1)
-        occ = 1;
+    const int cus = device_cus();
+    int occ = cached_occupancy(kernel, kBlock, lds);
     if (per_cu > 0 && occ > per_cu) occ = per_cu;
     const long cap = (long)occ * cus;
     if (g > cap) g = cap;
@@ -1210,15 +1213,13 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
         const int g = grid_for(k, lds, (long)a.N * S, RL, depth, per_cu);
         return (g + S - 1) / S;
     };
-    // ternary: the byte table shares the workgroup's LDS
-    constexpr size_t lut = (F == FMT_TERN && QMV_TERN_LUT) ? kTernLutBytes : 0;
     if (a.M == 1) {
         constexpr bool xreg = xreg_fits<F, NI>();
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, xreg>;
-        const size_t lds = (size_t)klen * 2 + lut;
+        const size_t lds = (size_t)klen * 2;
         hipLaunchKernelGGL(k, dim3(gx(k, lds, D * QMV_ROWS1, stream_per_cu<NI, 1>()), 1, S), dim3(kBlock), lds, st, wq, a.sc, a.x, a.y, a.y_dtype, a.M,
                            a.N, a.K, seg_split, a.part);
-    } else if (wide_fits(klen, 1, mc_wide<NI>()) && !(F == FMT_TERN && QMV_TERN_LUT)) {
+    } else if (wide_fits(klen, 1, mc_wide<NI>())) {
         constexpr int MCW = mc_wide<NI>();
         auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false>;
         const size_t lds = (size_t)MCW * klen * 2;
@@ -1227,7 +1228,7 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
                            a.x, a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
     } else {
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
-        const size_t lds = (size_t)klen * 2 + lut;
+        const size_t lds = (size_t)klen * 2;
         hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), a.M, S), dim3(kBlock), lds, st, wq, a.sc, a.x,
                            a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
     }

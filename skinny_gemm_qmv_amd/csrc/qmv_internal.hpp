@@ -6,7 +6,60 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace qmv {
+
+// Launch-shape facts computed on first use and kept: the CU count per
+// device, and per (device, kernel, block size, LDS bytes) the workgroups one
+// CU holds.  The values are fixed for a process, so a lookup only needs the
+// table's short lock (host code only).
+constexpr int kMaxDevices = 64;
+
+inline int current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    return dev;
+}
+
+inline int device_cus() {
+    static std::atomic<int> cache[kMaxDevices];
+    const int dev = current_device();
+    int cus = cache[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 256;
+        cache[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
+}
+
+template <class Kern>
+inline int cached_occupancy(Kern kernel, int block, size_t lds) {
+    struct Entry {
+        const void *k;
+        int dev, block;
+        size_t lds;
+        int occ;
+    };
+    static std::mutex mu;
+    static Entry table[512];
+    static int used = 0;
+    const void *key = reinterpret_cast<const void *>(kernel);
+    const int dev = current_device();
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < used; ++i)
+            if (table[i].k == key && table[i].dev == dev && table[i].block == block && table[i].lds == lds)
+                return table[i].occ;
+    }
+    int occ = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, lds) != hipSuccess || occ < 1) occ = 1;
+    std::lock_guard<std::mutex> g(mu);
+    if (used < 512) table[used++] = Entry{key, dev, block, lds, occ};
+    return occ;
+}
 
 // Per-row-group lane layout: RL lanes share one row, each lane owns the
 // segments j = q + RL*a (a < NI); NIP = lane-local tree width (power of two).

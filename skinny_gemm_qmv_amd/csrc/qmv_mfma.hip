@@ -258,9 +258,7 @@ static hipError_t mfma_nbw(const MatvecArgs &a, int NT, int mblocks, long slots,
 hipError_t launch_mxfp4_mfma(const MatvecArgs &a, hipStream_t st) {
     if (a.fmt != FMT_MXFP4 || a.M < 32 || a.M > 256 || a.K % 32 != 0) return hipErrorInvalidValue;
     const int NT = (a.N + 15) / 16;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int cus = device_cus();
     const int mt = (a.M + 15) / 16;
     constexpr int MTL = QMV_MFMA_MT_L;
     if (mt <= 2) return mfma_nbw<2, QMV_MFMA_DW_S>(a, NT, 1, cus, st);

@@ -648,6 +648,27 @@ def check_argmax_ties(lib):
     assert np.array_equal(mv, lg.max(axis=1))
 
 
+def check_no_contraction(lib):
+    """The arithmetic contract: every binary32 operation rounds on its own,
+    and nothing is fused unless written as fma.  (1 + 2^-12)^2 = 1 + 2^-11 +
+    2^-24 is a tie between two binary32 neighbours and rounds to the even one,
+    1 + 2^-11; adding -(1 + 2^-11) then gives exactly 0, while one fused
+    rounding would keep the 2^-24.  Both roundings are worked out exactly
+    here with rationals."""
+    from fractions import Fraction as Fr
+    a = 1.0 + 2.0 ** -12
+    c = -(1.0 + 2.0 ** -11)
+    exact = Fr(a) * Fr(a)
+    lo = Fr(1) + Fr(2) ** -11            # 1 + 2^-11: last significand bit 0
+    hi = lo + Fr(2) ** -23               # its upper neighbour
+    assert exact - lo == hi - exact       # a tie, resolved to the even lo
+    unfused = float(lo + Fr(c))
+    fused = float(exact + Fr(c))
+    assert unfused == 0.0 and fused == 2.0 ** -24
+    got = lib.orc_probe_mul_add(a, a, c)
+    assert got == unfused and math.copysign(1.0, got) == 1.0, got
+
+
 ALL_CHECKS = [
     check_f16_decode_all, check_f32_to_f16_rne, check_f64_to_f16_rne, check_f32_to_bf16_rne,
     check_bf16_decode, check_int2_decode, check_int4_decode, check_e2m1_table, check_pack_roundtrip,
@@ -656,4 +677,5 @@ ALL_CHECKS = [
     check_exp_accuracy, check_gelu_accuracy, check_rmsnorm_vs_fp64, check_fused_composition,
     check_qkv_composition, check_expert_gather, check_ternary_decode, check_ternary_vs_fp64,
     check_ternary_closed_form, check_quant_mxfp4, check_fused_quant_composition, check_argmax_ties,
+    check_no_contraction,
 ]

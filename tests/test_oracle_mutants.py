@@ -129,3 +129,62 @@ def test_unmutated_copy_passes(tmp_path):
     lib = oracle.load(obuild.build(str(src), str(tmp_path / "lib_copy.so"), (), quiet=True))
     for check in {m[4] for m in MUTANTS}:
         check(lib)
+
+
+# Build-flag mutants: the same source built with flags that break the
+# arithmetic contract.  Checked in a child process, because a shared object
+# built with -ffast-math may switch the whole process to flush-to-zero.
+FLAG_MUTANTS = [
+    ("fast_math", ("-ffast-math",)),                            # FTZ/DAZ, reassociation, no signed zeros
+    ("contraction_with_fma", ("-ffp-contract=fast", "-mfma")),  # a*b+c fused into one rounding
+]
+
+CHILD = r"""
+import json, os, sys
+sys.path[:0] = [os.environ["QMV_ROOT"], os.path.join(os.environ["QMV_ROOT"], "tests")]
+import oracle, oracle_pins as P
+lib = oracle.load(sys.argv[1])
+failed = []
+for check in P.ALL_CHECKS:
+    try:
+        check(lib)
+    except AssertionError:
+        failed.append(check.__name__)
+print(json.dumps(failed))
+"""
+
+
+def _pins_in_child(lib_path, env_extra=None, timeout=900):
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, QMV_ROOT=root, **(env_extra or {}))
+    r = subprocess.run([sys.executable, "-c", CHILD, lib_path], capture_output=True, text=True, timeout=timeout,
+                       env=env)
+    assert r.returncode == 0, r.stderr[-4000:]
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+@pytest.mark.parametrize("name,flags", FLAG_MUTANTS, ids=[m[0] for m in FLAG_MUTANTS])
+def test_flag_mutant_is_caught(tmp_path, name, flags):
+    lib = obuild.build(SRC, str(tmp_path / f"lib_{name}.so"), flags, quiet=True)
+    failed = _pins_in_child(lib)
+    assert failed, f"no pin rejected the oracle built with {flags}"
+
+
+def test_pins_pass_under_address_and_undefined_sanitizers(tmp_path):
+    """The oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any report aborts) passes every pin: no out-of-bounds access, no
+    undefined arithmetic anywhere the pins reach."""
+    import subprocess
+    libasan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                             check=True).stdout.strip()
+    if not os.path.isabs(libasan) or not os.path.exists(libasan):
+        pytest.skip("gcc has no AddressSanitizer runtime here")
+    flags = ("-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g")
+    lib = obuild.build(SRC, str(tmp_path / "lib_asan.so"), flags, quiet=True)
+    env = {"LD_PRELOAD": libasan, "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1",
+           "UBSAN_OPTIONS": "print_stacktrace=1:halt_on_error=1"}
+    failed = _pins_in_child(lib, env)
+    assert failed == [], failed
