@@ -24,7 +24,9 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE memory owned by the caller; the library
- *    keeps no pointer after the call returns and never allocates.
+ *    keeps no pointer after the call returns and never allocates
+ *    (qmv_int2_argmax_static uses a static device array of the library in
+ *    place of a workspace).
  *  - Row-major layouts.  fp16 and bf16 values are passed as uint16_t bit
  *    patterns.  Packed weights:
  *      int2  : uint32_t [N][K/16]; code k = 16w+i is bits 2i+1..2i of word w,
@@ -268,6 +270,21 @@ qmv_status qmv_int2_rmsnorm_qkv(const uint16_t *x, const uint16_t *residual, uin
 qmv_status qmv_int2_argmax(const uint32_t *wq, const uint16_t *scale, const uint16_t *x,
                            int32_t *idx, float *maxval, float *logits, int M, int N, int K,
                            qmv_mode mode, void *workspace, size_t ws_bytes, void *stream);
+
+/* qmv_int2_argmax without a workspace, for callers that cannot allocate
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and modes as qmv_int2_argmax; the
+ * counters and keys live in a static device array of the library (3 KB per
+ * GPU, kept until the process ends), whose address is taken once per device
+ * on the first call there (that call also clears it with a fill kernel on
+ * `stream`; every call leaves it zeroed).  Calls on one GPU share that array:
+ * calls that overlap in time on one GPU race and give wrong results (keep
+ * them on one stream, or ordered).  No allocation, no allocating library
+ * call.  QMV_ERR_WORKSPACE if M needs more than the array holds (it holds
+ * every M <= QMV_MAX_M). */
+qmv_status qmv_int2_argmax_static(const uint32_t *wq, const uint16_t *scale, const uint16_t *x,
+                                  int32_t *idx, float *maxval, float *logits, int M, int N, int K,
+                                  qmv_mode mode, void *stream);
 
 /* Expert-gather MXFP4 matvec ("raw-Metal loop playbook", next-target ranking
  * table: the gpt-oss MoE row, a zero-materialisation expert-gather matvec).

@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "qmv_int2", "qmv_int4", "qmm_mxfp4", "qmv_int2_rmsnorm_gateup_gelu", "qmv_int2_rmsnorm_qkv",
-    "qmv_int2_argmax", "qmm_mxfp4_gather", "qmv_ternary", "ternary_row_bytes",
+    "qmv_int2_argmax", "qmv_int2_argmax_static", "qmm_mxfp4_gather", "qmv_ternary", "ternary_row_bytes",
     "qmv_int2_rmsnorm_gateup_gelu_mxfp4", "qmv_quant_mxfp4", "workspace_size", "workspace_init", "fo_spec", "abi_version", "QmvError", "LIB_PATH",
     "MODES", "OPS",
 ]
@@ -52,6 +52,7 @@ _SIGS = {
     "qmv_int2_rmsnorm_gateup_gelu": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp,
                                       _i, _i, _i, _i, _vp, _sz, _vp], _i),
     "qmv_int2_argmax": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
+    "qmv_int2_argmax_static": ([_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp], _i),
     "qmv_int2_rmsnorm_qkv": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i,
                               _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp], _i),
     "qmv_int2_rmsnorm_gateup_gelu_mxfp4": ([_vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -335,4 +336,23 @@ def qmv_int2_argmax(wq, scale, x, idx=None, maxval=None, logits=None, want_maxva
     _check(_lib.qmv_int2_argmax(_ptr(wq), _ptr(scale), _ptr(x), _ptr(idx), _ptr(maxval),
                                 _ptr(logits), M, N, K, _mode(mode), _ptr(ws), wsb, _stream(stream)),
            "qmv_int2_argmax")
+    return idx, maxval, logits
+
+
+def qmv_int2_argmax_static(wq, scale, x, idx, maxval=None, logits=None, mode="fixed", stream=None):
+    """qmv_int2_argmax with the library's static scratch instead of a workspace
+    (see qmv.h); allocates nothing, so every output is the caller's:
+    idx int32 [M], maxval fp32 [M] or None, logits fp32 [M,N] or None."""
+    M, K = x.shape
+    N = wq.shape[0]
+    _req(wq, "wq", torch.int32, (N, K // 16))
+    _req(scale, "scale", torch.float16, (N,))
+    _req(x, "x", torch.float16, (M, K))
+    _req(idx, "idx", torch.int32, (M,))
+    if maxval is not None:
+        _req(maxval, "maxval", torch.float32, (M,))
+    if logits is not None:
+        _req(logits, "logits", torch.float32, (M, N))
+    _check(_lib.qmv_int2_argmax_static(_ptr(wq), _ptr(scale), _ptr(x), _ptr(idx), _ptr(maxval), _ptr(logits),
+                                       M, N, K, _mode(mode), _stream(stream)), "qmv_int2_argmax_static")
     return idx, maxval, logits

@@ -6,10 +6,22 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "qmv.h"
 #include "qmv_internal.hpp"
 
 namespace {
+
+// Scratch of qmv_int2_argmax_static: the argmax workspace (completion
+// counters, then one 64-bit key per activation row) for up to QMV_MAX_M
+// rows, in device memory the library owns, one copy per GPU for the life of
+// the process.  Host code never uses the name `scratch` as an address: each
+// device's address comes from hipGetSymbolAddress, taken once per device.
+constexpr size_t kStaticScratchBytes = 1024 + ((QMV_MAX_M * 8 + 255) / 256) * 256;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[qmv::kMaxDevices];
 
 thread_local char g_last_hip_error[256] = "";
 
@@ -275,6 +287,49 @@ qmv_status qmm_mxfp4_gather(const uint8_t *wq, const uint8_t *e8m0, int E, const
     if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
     qmv::GatherArgs a{wq, e8m0, x, idx, y, (int)y_dtype, E, topk, M, N, K};
     return hip_status(qmv::launch_fo_gather(a, static_cast<hipStream_t>(stream)));
+}
+
+// The calling thread's device's copy of `scratch` (taken and cleared on the
+// first call on that device; the argmax kernel leaves it zeroed after every
+// call).
+static qmv_status static_scratch(hipStream_t st, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= qmv::kMaxDevices) return QMV_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (p == nullptr) return QMV_ERR_HIP;
+        // device globals start zeroed; clear once more with a fill kernel
+        // (not a memset), on the caller's stream
+        e = qmv::launch_fill_zero(p, kStaticScratchBytes, st);
+        if (e != hipSuccess) return hip_status(e);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QMV_OK;
+}
+
+qmv_status qmv_int2_argmax_static(const uint32_t *wq, const uint16_t *scale, const uint16_t *x,
+                                  int32_t *idx, float *maxval, float *logits, int M, int N, int K,
+                                  qmv_mode mode, void *stream) {
+    if (!wq || !scale || !x || !idx) return QMV_ERR_INVALID_ARG;
+    if (!valid_shape(M, N, K, 64) || !valid_mode(mode)) return QMV_ERR_INVALID_ARG;
+    if (!fits_32bit(N, K, 4)) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(idx, 4) || (maxval && !aligned(maxval, 4)) ||
+        (logits && !aligned(logits, 4)))
+        return QMV_ERR_ALIGNMENT;
+    if (mode != QMV_MODE_FIXED) return QMV_ERR_UNSUPPORTED;
+    const size_t need = qmv::argmax_workspace_bytes(M, N, K);
+    if (need == 0 || need > kStaticScratchBytes) return QMV_ERR_WORKSPACE;  // beyond the static scratch
+    void *ws = nullptr;
+    const qmv_status s = static_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (s != QMV_OK) return s;
+    qmv::ArgmaxArgs a{wq, scale, x, idx, maxval, logits, M, N, K, ws};
+    return hip_status(qmv::launch_fo_argmax(a, static_cast<hipStream_t>(stream)));
 }
 
 qmv_status qmv_int2_argmax(const uint32_t *wq, const uint16_t *scale, const uint16_t *x,
