@@ -33,7 +33,8 @@
 //    L2, so the weight ring is the deep one).
 //  * The workgroup count is sized to cover the CUs once: M is split into
 //    ceil(M/16/MT) blocks and each wave takes up to four weight tiles, so
-//    every activation fragment read from LDS feeds several matrix ops.
+//    every activation fragment read from LDS feeds several matrix ops; with
+//    a single m-block the tile ranges are spread over every CU.
 #include "qmv_device.hpp"
 #include "qmv_internal.hpp"
 
@@ -240,13 +241,18 @@ static hipError_t mfma_launch(const MatvecArgs &a, int NT, int ranges, int mbloc
 }
 
 // Weight tiles per wave: the fewest (at most four) that keep the workgroups
-// (ranges x m-blocks) within `per_cu` per CU.  More tiles per wave means more
-// matrix ops per activation fragment read from LDS.
+// (ranges x m-blocks) within `slots`.  More tiles per wave means more matrix
+// ops per activation fragment read from LDS.  With one m-block the ranges
+// are then spread over every slot (one per CU): more ranges only shorten
+// them, so none spans more than 4 * nbw tiles, and the per-CU share of the
+// weights drops from 4 * nbw tiles to NT / CUs (measured on MI355X at
+// N = 21504, K = 5376: M = 32 29.9 -> 27.6 us, M = 64 38.0 -> 37.2 us).
 template <int MT, int DW>
 static hipError_t mfma_nbw(const MatvecArgs &a, int NT, int mblocks, long slots, hipStream_t st) {
     int nbw = 1;
     while (nbw < 4 && (long)((NT + 4 * nbw - 1) / (4 * nbw)) * mblocks > slots) ++nbw;
-    const int ranges = (NT + 4 * nbw - 1) / (4 * nbw);  // every range spans <= 4 * nbw tiles
+    int ranges = (NT + 4 * nbw - 1) / (4 * nbw);  // every range spans <= 4 * nbw tiles
+    if (mblocks == 1 && ranges < slots) ranges = (int)(NT < slots ? NT : slots);
     if (nbw == 1) return mfma_launch<MT, 1, DW>(a, NT, ranges, mblocks, st);
     if (nbw == 2) return mfma_launch<MT, 2, DW>(a, NT, ranges, mblocks, st);
     if (nbw == 3) return mfma_launch<MT, 3, DW>(a, NT, ranges, mblocks, st);
