@@ -56,6 +56,12 @@ HEAD_N, HEAD_K = 262144, 1536
 HEAD_LABEL = "int2 lm_head+argmax N=262144 K=1536 M=1"
 HEAD_TRAFFIC = "int2_argmax_n262144_k1536_m1_traffic.json"
 EXTRA_STEPS = 200  # timed calls per extra workload (the headline times exactly --steps)
+# The pages' figure for the same metric on the same workload (the int2 lm_head
+# matvec, K = 1536, a vocab-sized stream of about 100 MB): 40.6 GB/s effective,
+# DRAM-bound, measured on another machine (Apple A19, Metal) -- context for
+# vs_baseline, not a target ("Gemma4 raw-Metal loop on A19", "What moved the
+# needle").
+PAGES_LM_HEAD_GBS = 40.6
 
 
 def effective_gbps(bytes_per_call, seconds_per_call):
@@ -632,7 +638,10 @@ def main(argv=None):
         "ms_per_step": sec * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": round(gbs / PAGES_LM_HEAD_GBS, 2),
+        "baseline": {"value": PAGES_LM_HEAD_GBS, "unit": "GB/s", "hardware": "Apple A19 (Metal)",
+                     "workload": "int2 lm_head matvec, K=1536, vocab-sized (~100 MB) stream, M=1",
+                     "note": "the pages' figure on another machine: context, not a target"},
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "int2 lm_head matvec N=262144, K=1536 (per-row fp16 scales, fp16 x) + single-pass "
