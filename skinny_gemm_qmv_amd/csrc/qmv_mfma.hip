@@ -269,7 +269,11 @@ hipError_t launch_mxfp4_mfma(const MatvecArgs &a, hipStream_t st) {
     constexpr int MTL = QMV_MFMA_MT_L;
     if (mt <= 2) return mfma_nbw<2, QMV_MFMA_DW_S>(a, NT, 1, cus, st);
     if (mt <= 4) return mfma_nbw<4, QMV_MFMA_DW_S>(a, NT, 1, cus, st);
-    return mfma_nbw<MTL, QMV_MFMA_DW_L>(a, NT, (mt + MTL - 1) / MTL, 2L * cus, st);
+    // two m-blocks: one workgroup per CU (N = 21504, K = 5376, M = 96 / 128:
+    // 51.1 / 52.5 us against 53.3 / 56.4 with two per CU); three or four: two
+    // per CU (one per CU measured 71 / 98 us against 69 / 86 at M = 192 / 256)
+    const int mblocks = (mt + MTL - 1) / MTL;
+    return mfma_nbw<MTL, QMV_MFMA_DW_L>(a, NT, mblocks, (mblocks <= 2 ? 1L : 2L) * cus, st);
 }
 
 }  // namespace qmv
