@@ -16,7 +16,8 @@ Measurement:
   * cold weights: the calls rotate over enough copies of the weights
     (>= 1 GiB) that no call finds its weights in the 256 MB last-level cache;
     the timed calls continue the rotation where the warmup calls stopped;
-  * the W warmup calls and the K timed calls are each captured once in a HIP
+  * the W warmup calls (default 500, so the clocks have settled under load)
+    and the K timed calls are each captured once in a HIP
     graph (torch.cuda.CUDAGraph) and replayed, so host launch cost stays out
     of the timed region; HIP events bracket the timed replay on the stream
     the kernels run on;
@@ -97,8 +98,11 @@ def gather_bytes(ids, E, N, K, M, topk):
 def parse(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=1000)
+    # about 16 ms of load before the timed calls: on MI355X the headline's
+    # time per call settles only after several ms of sustained load (200
+    # calls measured 35-37 us after 20 warmup calls, 32.2 us after 500)
+    p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--no-extra", action="store_true", help="skip the sweep over the other workloads")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
     p.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling and dispatch floor")
@@ -158,15 +162,20 @@ def rotating(t, copies):
     return [t] + [t.clone() for _ in range(copies - 1)]
 
 
-def run_case(make_call, steps, warmup):
+def run_case(make_call, steps, warmup, min_warm_s=0.0):
     """make_call(i) -> callable for step i.  The warmup calls are steps
     0 .. W-1 and the timed calls W .. W+K-1, so a rotation over weight copies
-    continues past the warmup instead of re-reading what it just read.
+    continues past the warmup instead of re-reading what it just read.  With
+    min_warm_s > 0 the warmup graph is replayed until that much GPU time has
+    passed (each replay ends at step W-1, so the rotation still continues
+    into the timed calls): the clocks settle only after several ms of load.
     Returns seconds per timed call."""
     wg = graph_of([make_call(i) for i in range(warmup)]) if warmup > 0 else None
     tg = graph_of([make_call(warmup + i) for i in range(steps)])
     if wg is not None:
-        time_graph(wg)
+        warm = time_graph(wg)
+        while warm < min_warm_s:
+            warm += time_graph(wg)
     return time_graph(tg) / steps
 
 
@@ -605,7 +614,9 @@ def main(argv=None):
             mk, nb, fl, bound = b()
             # at least EXTRA_STEPS calls per timed graph, so that the graph
             # launch does not inflate the latency-floor kernels (a few us each)
-            s = run_case(mk, max(EXTRA_STEPS, args.steps // 10), max(5, args.warmup // 4))
+            # the inputs are generated on the host first, so the GPU has idled:
+            # warm up for at least 20 ms of load
+            s = run_case(mk, max(EXTRA_STEPS, args.steps // 10), max(5, args.warmup // 4), min_warm_s=0.02)
             rec = {"workload": label, "us_per_call": round(s * 1e6, 3),
                    "GB/s": round(effective_gbps(nb, s), 1),
                    "TFLOP/s": round(fl / s / 1e12, 3), "bound": bound,
