@@ -194,7 +194,7 @@ __device__ __forceinline__ float seg_scale(uint32_t bits) {
 // R > 1 (used with several activation columns read from LDS): every
 // activation value read (and widened) is used for R rows, which divides the
 // LDS traffic and conversion work per multiply-add by R.
-template <int F, int RL, int NI, int NIP, int MC, bool XREG, int NMAT, int D, int R>
+template <int F, int RL, int NI, int NIP, int MC, bool XREG, int NMAT, int D, int R, int WV = kWaves>
 struct FoEngine {
     static constexpr int CODES = SegCodes<F>::v;
     static constexpr int XV = CODES / 8;  // 16-byte activation vectors per segment per column
@@ -261,10 +261,10 @@ struct FoEngine {
         row_bytes = (uint32_t)nseg_row * 16u;
         const int total_rg = (N + RPG - 1) / RPG;
         total_units = (total_rg + R - 1) / R;
-        stride = nblk * kWaves;
+        stride = nblk * WV;
         // wave-uniform: read it through a scalar so that the unit loop is a
         // scalar loop (no exec-masked control flow around the load ring)
-        first = __builtin_amdgcn_readfirstlane(blk * kWaves + wave);
+        first = __builtin_amdgcn_readfirstlane(blk * WV + wave);
         // bytes of scale data per row
         srow = kRowScale<F> ? 2u : (F == FMT_INT4 ? 2u * nseg_row : (uint32_t)nseg_row);
         const uint32_t ssz = F == FMT_INT2 ? 2u : (F == FMT_INT4 ? 2u : 1u);  // bytes per scale
@@ -644,8 +644,8 @@ struct StoreEpi {
 // blockIdx.z selects a K split of seg_split segments (one split covering the
 // whole row in fixed-order mode, part == nullptr); split z writes its partial
 // sums to part + z*M*N.
-template <int F, int RL, int NI, int NIP, int MC, bool XREG>
-__global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict__ wq,
+template <int F, int RL, int NI, int NIP, int MC, bool XREG, int WV = kWaves>
+__global__ __launch_bounds__(64 * WV) void k_fo_matvec(const uint8_t *__restrict__ wq,
                                                       const void *__restrict__ sc,
                                                       const uint16_t *__restrict__ x, void *y,
                                                       int y_dtype, int M, int N, int K, int seg_split,
@@ -662,8 +662,8 @@ __global__ __launch_bounds__(kBlock) void k_fo_matvec(const uint8_t *__restrict_
     const uint16_t *xz = x + (size_t)seg0 * CODES;
     const uint8_t *const w1[1] = {wq};
     const void *const s1[1] = {sc};
-    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG, F>()> eng(w1, s1, N, klen, seg0,
-                                                                                       nseg_row);
+    FoEngine<F, RL, NI, NIP, MC, XREG, 1, ring_depth<NI, 1>(), rows_block<MC, XREG, F>(), WV> eng(
+        w1, s1, N, klen, seg0, nseg_row);
     XStage<MC> xst;
     xst.load(xz, M, K, klen, m0, kval);
     eng.prefetch();
@@ -1129,12 +1129,13 @@ __global__ void k_fill_zero(uint32_t *p, size_t words) {
 // `per_cu` (if > 0) caps the resident workgroups per CU below what occupancy
 // allows.  A full launch then has the same number of workgroups on every CU.
 template <class Kern>
-static int grid_for(Kern kernel, size_t lds, long N, int RL, int depth, int per_cu = 0) {
+static int grid_for(Kern kernel, size_t lds, long N, int RL, int depth, int per_cu = 0, int block = kBlock) {
     const int rpg = 64 / RL;
+    const int waves = block / 64;
     const long total_rg = ((long)N + rpg - 1) / rpg;
-    long g = (total_rg + (long)kWaves * depth - 1) / ((long)kWaves * depth);
+    long g = (total_rg + (long)waves * depth - 1) / ((long)waves * depth);
     const int cus = device_cus();
-    int occ = cached_occupancy(kernel, kBlock, lds);
+    int occ = cached_occupancy(kernel, block, lds);
     if (per_cu > 0 && occ > per_cu) occ = per_cu;
     const long cap = (long)occ * cus;
     if (g > cap) g = cap;
@@ -1184,6 +1185,14 @@ constexpr int mc_wide() {
 #endif
 constexpr int kWideUnits = QMV_WIDE_UNITS;
 
+// Waves per workgroup of the several-column matvec: eight for int4 (half
+// the workgroups, so each CU stages its activation chunk once instead of
+// twice: N=16384, K=4096, M = 4 / 8 / 16 took 18.8 / 32.6 / 57.7 us against
+// 20.1 / 33.8 / 59.0 with four), four for the other formats (MXFP4 M = 16 /
+// 64 measured 7 % slower with eight).
+template <int F>
+constexpr int kWideWaves = F == FMT_INT4 ? 8 : kWaves;
+
 // Registers a lane spends on its activation slice when MC = 1 (16-byte
 // vectors x 4 VGPRs); above this budget the slice is read from LDS instead.
 constexpr int kXregBudget = QMV_XREG_BUDGET;
@@ -1209,8 +1218,8 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
     const int S = a.splits > 0 ? a.splits : 1;
     const int klen = seg_split * CODES;  // activation values staged per column
     // workgroups along x for one split: sized as if the S splits were S*N rows
-    auto gx = [&](auto k, size_t lds, int depth, int per_cu = 0) {
-        const int g = grid_for(k, lds, (long)a.N * S, RL, depth, per_cu);
+    auto gx = [&](auto k, size_t lds, int depth, int per_cu = 0, int block = kBlock) {
+        const int g = grid_for(k, lds, (long)a.N * S, RL, depth, per_cu, block);
         return (g + S - 1) / S;
     };
     if (a.M == 1) {
@@ -1221,11 +1230,12 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
                            a.N, a.K, seg_split, a.part);
     } else if (wide_fits(klen, 1, mc_wide<NI>())) {
         constexpr int MCW = mc_wide<NI>();
-        auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false>;
+        constexpr int WV = kWideWaves<F>;
+        auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false, WV>;
         const size_t lds = (size_t)MCW * klen * 2;
         const int gy = (a.M + MCW - 1) / MCW;
-        hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS), gy, S), dim3(kBlock), lds, st, wq, a.sc,
-                           a.x, a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
+        hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS, 0, 64 * WV), gy, S), dim3(64 * WV), lds, st, wq,
+                           a.sc, a.x, a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
     } else {
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
         const size_t lds = (size_t)klen * 2;
