@@ -1185,13 +1185,18 @@ constexpr int mc_wide() {
 #endif
 constexpr int kWideUnits = QMV_WIDE_UNITS;
 
-// Waves per workgroup of the several-column matvec: eight for int4 (half
-// the workgroups, so each CU stages its activation chunk once instead of
-// twice: N=16384, K=4096, M = 4 / 8 / 16 took 18.8 / 32.6 / 57.7 us against
-// 20.1 / 33.8 / 59.0 with four), four for the other formats (MXFP4 M = 16 /
-// 64 measured 7 % slower with eight).
+// Waves per workgroup and units per wave of the several-column matvec: for
+// int4 eight waves of one unit each (each CU then stages its activation
+// chunk once instead of twice, with twice the resident waves: N=16384,
+// K=4096, M = 4 / 8 / 16 took 18.8 / 32.6 / 57.7 us with eight waves of two
+// units against 20.1 / 33.8 / 59.0 with four, and one unit each took
+// another 4-5 % off M = 4 and 8 on two boxes: 17.9 / 29.4 against 18.8 /
+// 30.7, M = 16 within +-2 %); four waves of kWideUnits for the other
+// formats (MXFP4 M = 16 / 64 measured 7 % slower with eight waves).
 template <int F>
 constexpr int kWideWaves = F == FMT_INT4 ? 8 : kWaves;
+template <int F>
+constexpr int kWideUnitsF = F == FMT_INT4 ? 1 : kWideUnits;
 
 // Registers a lane spends on its activation slice when MC = 1 (16-byte
 // vectors x 4 VGPRs); above this budget the slice is read from LDS instead.
@@ -1234,7 +1239,7 @@ static hipError_t fo_matvec_shape(const MatvecArgs &a, hipStream_t st) {
         auto k = k_fo_matvec<F, RL, NI, NIP, MCW, false, WV>;
         const size_t lds = (size_t)MCW * klen * 2;
         const int gy = (a.M + MCW - 1) / MCW;
-        hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnits * QMV_ROWS, 0, 64 * WV), gy, S), dim3(64 * WV), lds, st, wq,
+        hipLaunchKernelGGL(k, dim3(gx(k, lds, kWideUnitsF<F> * QMV_ROWS, 0, 64 * WV), gy, S), dim3(64 * WV), lds, st, wq,
                            a.sc, a.x, a.y, a.y_dtype, a.M, a.N, a.K, seg_split, a.part);
     } else {
         auto k = k_fo_matvec<F, RL, NI, NIP, 1, false>;
