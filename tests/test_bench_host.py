@@ -76,6 +76,21 @@ def test_timed_rotation_continues_after_the_warmup(monkeypatch):
     assert sec == 1.0 / 7
 
 
+def test_warmup_replays_until_the_minimum_load_time(monkeypatch):
+    """min_warm_s replays the warmup graph (steps 0 .. W-1 each time, so the
+    rotation still continues into the timed calls) until that much GPU time
+    has passed; the timed graph is replayed exactly once."""
+    replays = []
+    monkeypatch.setattr(bench, "graph_of", lambda calls: ("warm" if len(calls) == 3 else "timed", calls))
+    monkeypatch.setattr(bench, "time_graph", lambda g: replays.append(g[0]) or (0.004 if g[0] == "warm" else 0.5))
+    sec = bench.run_case(lambda i: (lambda: None), steps=5, warmup=3, min_warm_s=0.01)
+    assert replays == ["warm", "warm", "warm", "timed"]   # 4 + 4 + 4 ms >= 10 ms
+    assert sec == 0.5 / 5
+    replays.clear()
+    bench.run_case(lambda i: (lambda: None), steps=5, warmup=3)
+    assert replays == ["warm", "timed"]                     # the headline: exactly W warmup calls
+
+
 def test_default_run_is_bounded():
     a = bench.parse([])
-    assert a.gpus == 1 and a.steps * 37e-6 < 60 and a.warmup < a.steps
+    assert a.gpus == 1 and (a.steps + a.warmup) * 40e-6 < 60 and a.warmup < a.steps
