@@ -70,14 +70,39 @@ def effective_gbps(bytes_per_call, seconds_per_call):
     return bytes_per_call / seconds_per_call / 1e9
 
 
+def strip_comments(src):
+    """C/C++ source text without its comments (string and character literals
+    kept), every run of whitespace folded to one space."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest():
-    """Digest of the product library's HIP sources, to tell whether stored
-    counter readings still describe the kernels being timed."""
+    """Digest of the product library's HIP sources, comments left out, to tell
+    whether stored counter readings still describe the kernels being timed."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "skinny_gemm_qmv_amd", "csrc")
     for name in DIGEST_FILES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

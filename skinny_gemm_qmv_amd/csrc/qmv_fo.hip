@@ -1186,13 +1186,14 @@ constexpr int mc_wide() {
 constexpr int kWideUnits = QMV_WIDE_UNITS;
 
 // Waves per workgroup and units per wave of the several-column matvec: for
-// int4 eight waves of one unit each (each CU then stages its activation
-// chunk once instead of twice, with twice the resident waves: N=16384,
-// K=4096, M = 4 / 8 / 16 took 18.8 / 32.6 / 57.7 us with eight waves of two
-// units against 20.1 / 33.8 / 59.0 with four, and one unit each took
-// another 4-5 % off M = 4 and 8 on two boxes: 17.9 / 29.4 against 18.8 /
-// 30.7, M = 16 within +-2 %); four waves of kWideUnits for the other
-// formats (MXFP4 M = 16 / 64 measured 7 % slower with eight waves).
+// int4 eight waves of one unit each, i.e. as many workgroups (two per CU,
+// each staging its activation chunk once) as four waves of two units, with
+// twice the resident waves (four per SIMD).  N=16384, K=4096, M = 4 / 8 /
+// 16: eight waves of two units (one workgroup per CU) took 18.8 / 32.6 /
+// 57.7 us against 20.1 / 33.8 / 59.0 with four, and eight waves of one unit
+// another 4-5 % less at M = 4 and 8 on two boxes (17.9 / 29.4 against 18.8 /
+// 30.7; M = 16 within +-2 %).  The other formats keep four waves of
+// kWideUnits (MXFP4 M = 16 / 64 measured 7 % slower with eight waves).
 template <int F>
 constexpr int kWideWaves = F == FMT_INT4 ? 8 : kWaves;
 template <int F>

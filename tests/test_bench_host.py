@@ -38,6 +38,14 @@ def test_source_digest_is_stable_and_hex():
     assert a == b and len(a) == 16 and int(a, 16) >= 0
 
 
+def test_digest_ignores_comments_but_not_code():
+    src = 'int a = 1; // one\n/* two\n lines */ const char *s = "x // y";\n'
+    same = '// a new note\nint a = 1;   /* changed */\nconst char *s = "x // y";\n'
+    assert bench.strip_comments(src) == bench.strip_comments(same)
+    assert bench.strip_comments(src) != bench.strip_comments(src.replace("a = 1", "a = 2"))
+    assert bench.strip_comments(src) != bench.strip_comments(src.replace("x // y", "x // z"))  # in a string
+
+
 def test_stored_traffic_follows_the_digest(tmp_path, monkeypatch):
     rec = {"source_digest": "0123456789abcdef", "hbm_bytes_per_launch": 12345}
     (tmp_path / "t.json").write_text(json.dumps(rec))
