@@ -1,0 +1,88 @@
+"""GPU: seeded random shapes through every fixed-order launch path, bit for bit
+against the oracle, and the matrix-core mode against the summation bound.
+
+The shapes are drawn once from a fixed seed (so a failure names a shape that
+reproduces): formats int2 / int4 / MXFP4, M from 1 to 256 (one-column
+streaming kernels, several-column kernels with their workgroup sizes, both
+K-split granularities), ragged N and every K granularity the formats allow.
+Each case stays small enough for the oracle to finish in well under a
+second."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_bits_equal, bits, dev
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("skinny_gemm_qmv_amd")
+
+_G = np.random.default_rng(20261203)
+
+
+def _draw(n):
+    cases = []
+    for _ in range(n):
+        fmt = ["int2", "int4", "mxfp4"][int(_G.integers(0, 3))]
+        M = int(_G.choice([1, 1, 2, 3, 4, 5, 8, 9, 16, 17, 31, 32, 33, 64, 100, 128, 200, 256]))
+        unit = 64 if fmt == "int2" else 32
+        K = unit * int(_G.integers(1, 8193 // unit if M <= 16 else 2049 // unit))
+        budget = 6_000_000 // (M * K) + 1          # keep M*N*K small for the oracle
+        N = int(_G.integers(1, max(2, min(5000, budget))))
+        cases.append((fmt, M, N, K, int(_G.integers(0, 1 << 30))))
+    return cases
+
+
+CASES = _draw(120)
+
+
+def _inputs(fmt, M, N, K, salt):
+    if fmt == "int2":
+        return synth.int2_inputs(M, N, K, salt=salt)
+    if fmt == "int4":
+        return synth.int4_inputs(M, N, K, salt=salt)
+    return synth.mxfp4_inputs(M, N, K, salt=salt)
+
+
+def _gpu(fmt, d, mode="fixed"):
+    if fmt == "int2":
+        y = q.qmv_int2(dev(d["wq"], "u32"), dev(d["scale"], "f16"), dev(d["x"], "f16"))
+    elif fmt == "int4":
+        y = q.qmv_int4(dev(d["wq"], "u32"), dev(d["scales"], "f16"), dev(d["x"], "f16"))
+    else:
+        y = q.qmm_mxfp4(dev(d["wq"], "u8"), dev(d["e8m0"], "u8"), dev(d["x"], "bf16"), mode=mode)
+    torch.cuda.synchronize()
+    return y
+
+
+def _oracle(fmt, d):
+    if fmt == "int2":
+        return oracle.qmv_int2(d["wq"], d["scale"], d["x"])
+    if fmt == "int4":
+        return oracle.qmv_int4(d["wq"], d["scales"], d["x"])
+    return oracle.qmm_mxfp4(d["wq"], d["e8m0"], d["x"])
+
+
+@pytest.mark.parametrize("fmt,M,N,K,salt", CASES, ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in CASES])
+def test_random_shape_fixed_order(fmt, M, N, K, salt):
+    d = _inputs(fmt, M, N, K, salt)
+    assert_bits_equal(bits(_gpu(fmt, d)), _oracle(fmt, d).view(np.uint32), f"{fmt} M={M} N={N} K={K}")
+
+
+MFMA_CASES = [c for c in CASES if c[0] == "mxfp4" and c[1] >= 32]
+
+
+@pytest.mark.parametrize("fmt,M,N,K,salt", MFMA_CASES, ids=[f"M{c[1]}-N{c[2]}-K{c[3]}" for c in MFMA_CASES])
+def test_random_shape_matrix_cores(fmt, M, N, K, salt):
+    """Matrix-core mode: every output within the fp32 summation bound of the
+    exact value (the weights dequantize exactly to bf16, so every product is
+    exact and only the order of the K additions differs)."""
+    d = _inputs(fmt, M, N, K, salt)
+    y = _gpu(fmt, d, mode="mfma").cpu().numpy().astype(np.float64)
+    exact, mag = oracle.ref64_mxfp4(d["wq"], d["e8m0"], d["x"])
+    u = 2.0 ** -24
+    gamma = K * u / (1.0 - K * u)
+    bad = np.argwhere(np.abs(y - exact) > gamma * mag + 1e-38)
+    assert bad.size == 0, f"M={M} N={N} K={K}: {len(bad)} outputs outside the bound, first {bad[0]}"
