@@ -86,3 +86,36 @@ def test_random_shape_matrix_cores(fmt, M, N, K, salt):
     gamma = K * u / (1.0 - K * u)
     bad = np.argwhere(np.abs(y - exact) > gamma * mag + 1e-38)
     assert bad.size == 0, f"M={M} N={N} K={K}: {len(bad)} outputs outside the bound, first {bad[0]}"
+
+
+def _draw_argmax_ternary(n):
+    cases = []
+    for _ in range(n):
+        kind = ["argmax", "ternary"][int(_G.integers(0, 2))]
+        M = int(_G.choice([1, 1, 2, 3, 4, 5, 8]))
+        K = (64 if kind == "argmax" else 8) * int(_G.integers(1, (4097 // 64) if kind == "argmax" else 1025))
+        N = int(_G.integers(1, max(2, min(30000, 8_000_000 // (M * K) + 1))))
+        cases.append((kind, M, N, K, int(_G.integers(0, 1 << 30))))
+    return cases
+
+
+EXTRA = _draw_argmax_ternary(40)
+
+
+@pytest.mark.parametrize("kind,M,N,K,salt", EXTRA, ids=[f"{c[0]}-M{c[1]}-N{c[2]}-K{c[3]}" for c in EXTRA])
+def test_random_shape_argmax_and_ternary(kind, M, N, K, salt):
+    if kind == "argmax":
+        d = synth.argmax_inputs(M, N, K, salt=salt)
+        idx, mv, lg = q.qmv_int2_argmax(dev(d["wq"], "u32"), dev(d["scale"], "f16"), dev(d["x"], "f16"),
+                                        want_logits=True)
+        torch.cuda.synchronize()
+        ri, rm, rl = oracle.int2_argmax(d["wq"], d["scale"], d["x"])
+        assert_bits_equal(bits(lg), rl.view(np.uint32), f"argmax logits M={M} N={N} K={K}")
+        assert np.array_equal(idx.cpu().numpy(), ri), f"argmax index M={M} N={N} K={K}"
+        assert_bits_equal(bits(mv), rm.view(np.uint32), f"argmax maximum M={M} N={N} K={K}")
+    else:
+        d = synth.ternary_inputs(M, N, K, salt=salt)
+        y = q.qmv_ternary(dev(d["wq"], "u8"), dev(d["scale"], "f16"), dev(d["x"], "f16"))
+        torch.cuda.synchronize()
+        assert_bits_equal(bits(y), oracle.qmv_ternary(d["wq"], d["scale"], d["x"]).view(np.uint32),
+                          f"ternary M={M} N={N} K={K}")
