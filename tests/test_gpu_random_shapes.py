@@ -119,3 +119,74 @@ def test_random_shape_argmax_and_ternary(kind, M, N, K, salt):
         torch.cuda.synchronize()
         assert_bits_equal(bits(y), oracle.qmv_ternary(d["wq"], d["scale"], d["x"]).view(np.uint32),
                           f"ternary M={M} N={N} K={K}")
+
+
+def _draw_fused(n):
+    cases = []
+    for _ in range(n):
+        kind = ["gateup", "gateup_mxfp4", "qkv", "gather"][int(_G.integers(0, 4))]
+        M = int(_G.choice([1, 1, 1, 2, 3, 4, 5, 9]))
+        if kind == "gather":
+            K = 32 * int(_G.integers(1, 257))
+            E = int(_G.integers(1, 9))
+            topk = int(_G.integers(1, E + 1))
+            N = int(_G.integers(1, max(2, min(3000, 4_000_000 // (M * topk * K) + 1))))
+            cases.append((kind, M, (E, topk, N), K, int(_G.integers(0, 1 << 30))))
+            continue
+        K = 64 * int(_G.integers(1, 129))
+        if kind == "qkv":
+            shape = tuple(int(v) for v in _G.integers(1, max(2, min(2000, 2_000_000 // (M * K) + 1)), size=3))
+        else:
+            N = int(_G.integers(1, max(2, min(4000, 3_000_000 // (M * K) + 1))))
+            shape = (32 * max(1, N // 32),) if kind == "gateup_mxfp4" else (N,)
+        cases.append((kind, M, shape, K, int(_G.integers(0, 1 << 30))))
+    return cases
+
+
+FUSED = _draw_fused(40)
+
+
+@pytest.mark.parametrize("kind,M,shape,K,salt", FUSED,
+                         ids=[f"{c[0]}-M{c[1]}-N{'x'.join(map(str, c[2]))}-K{c[3]}" for c in FUSED])
+def test_random_shape_fused(kind, M, shape, K, salt):
+    if kind == "gather":
+        E, topk, N = shape
+        d = synth.expert_inputs(M, E, topk, N, K, salt=salt)
+        ids = torch.from_numpy(np.ascontiguousarray(d["idx"], np.int32)).cuda()
+        y = q.qmm_mxfp4_gather(dev(d["wq"], "u8"), dev(d["e8m0"], "u8"), dev(d["x"], "bf16"), ids)
+        torch.cuda.synchronize()
+        want = oracle.qmm_mxfp4_gather(d["wq"], d["e8m0"], d["x"], d["idx"])
+        assert_bits_equal(bits(y), want.view(np.uint32), f"gather M={M} E={E} topk={topk} N={N} K={K}")
+        return
+    if kind == "qkv":
+        d = synth.qkv_inputs(M, *shape, K, salt=salt)
+        res = torch.empty((M, K), dtype=torch.float16, device="cuda")
+        ys = q.qmv_int2_rmsnorm_qkv(dev(d["x"], "f16"), dev(d["residual"], "f16"), dev(d["gamma"], "f16"),
+                                    d["eps"], dev(d["wq_q"], "u32"), dev(d["s_q"], "f16"), dev(d["wq_k"], "u32"),
+                                    dev(d["s_k"], "f16"), dev(d["wq_v"], "u32"), dev(d["s_v"], "f16"),
+                                    residual_out=res)
+        torch.cuda.synchronize()
+        want = oracle.int2_rmsnorm_qkv(d["x"], d["residual"], d["gamma"], d["eps"], d["wq_q"], d["s_q"],
+                                       d["wq_k"], d["s_k"], d["wq_v"], d["s_v"])
+        for z in range(3):
+            assert_bits_equal(bits(ys[z]), want[z].view(np.uint32), f"q/k/v {z} M={M} N={shape} K={K}")
+        assert np.array_equal(res.cpu().view(torch.int16).numpy().view(np.uint16), want[3])
+        return
+    (N,) = shape
+    d = synth.fused_inputs(M, N, K, salt=salt)
+    a = (dev(d["x"], "f16"), dev(d["residual"], "f16"), dev(d["gamma"], "f16"), d["eps"],
+         dev(d["wq_gate"], "u32"), dev(d["s_gate"], "f16"), dev(d["wq_up"], "u32"), dev(d["s_up"], "f16"))
+    o = (d["x"], d["residual"], d["gamma"], d["eps"], d["wq_gate"], d["s_gate"], d["wq_up"], d["s_up"])
+    res = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    if kind == "gateup":
+        out = q.qmv_int2_rmsnorm_gateup_gelu(*a, residual_out=res)
+        torch.cuda.synchronize()
+        wo, wr, _, _ = oracle.int2_rmsnorm_gateup_gelu(*o)
+        assert_bits_equal(bits(out), wo, f"gate/up M={M} N={N} K={K}")
+    else:
+        codes, e8 = q.qmv_int2_rmsnorm_gateup_gelu_mxfp4(*a, residual_out=res)
+        torch.cuda.synchronize()
+        wc, we, wr = oracle.int2_rmsnorm_gateup_gelu_mxfp4(*o)
+        assert np.array_equal(e8.cpu().numpy(), we), f"E8M0 M={M} N={N} K={K}"
+        assert np.array_equal(codes.cpu().numpy(), wc), f"codes M={M} N={N} K={K}"
+    assert np.array_equal(res.cpu().view(torch.int16).numpy().view(np.uint16), wr), f"residual_out M={M} K={K}"
