@@ -31,6 +31,12 @@
 //  * Weight loads run DW chunks ahead and activation loads DX chunks ahead
 //    in registers (the weights come from HBM, the activations mostly from
 //    L2, so the weight ring is the deep one).
+//  * Block scales: when K is a multiple of 128 (every chunk whole, so a
+//    row's scale bytes start on a dword), one 16-byte load per tile brings
+//    the scales of four chunks (blocks 16G .. 16G+15 of the row) and lane
+//    group g takes byte g of dword c % 4; otherwise each chunk loads its
+//    scale byte per lane.  A vector-memory instruction costs about the
+//    same whatever its width, and the byte loads were a quarter of them.
 //  * The workgroup count is sized to cover the CUs once: M is split into
 //    ceil(M/16/MT) blocks and each wave takes up to four weight tiles, so
 //    every activation fragment read from LDS feeds several matrix ops; with
@@ -48,7 +54,7 @@ constexpr uint32_t kOob = 0xFFFFFFF0u;  // past every buffer: loads return 0
 constexpr int kXRow = 128 * 2 + 16;     // LDS bytes per activation row of a chunk (+16: bank spread)
 constexpr int kMfmaThreads = 256;
 
-template <int MT, int NBW, int DW, int DX>
+template <int MT, int NBW, int DW, int DX, bool SV>
 __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__restrict__ wq,
                                                              const uint8_t *__restrict__ e8m0,
                                                              const uint16_t *__restrict__ x, void *y,
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__re
 
     // weight tiles of this wave: the s-th is tile t0 + wave + 4s (rows past
     // N and tiles past the range read zeros)
-    uint32_t wrow[NBW], erow[NBW];
+    uint32_t wrow[NBW], erow[NBW], erow0[NBW];
     bool tok[NBW];
 #pragma unroll
     for (int s = 0; s < NBW; ++s) {
@@ -83,7 +89,8 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__re
         tok[s] = t < t1;
         const uint32_t n = (uint32_t)t * 16u + r16;
         wrow[s] = n * row_bytes + 16u * g;
-        erow[s] = n * (uint32_t)nseg + g;
+        erow0[s] = n * (uint32_t)nseg;
+        erow[s] = erow0[s] + g;
     }
     // activation pieces of this lane: piece p = threadIdx.x + 256 i is row
     // p / 16, 16-byte column p % 16 of the workgroup's chunk
@@ -100,6 +107,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__re
     }
 
     static_assert(DW % DX == 0, "the unrolled loop cycles both rings");
+    static_assert(!SV || DW == 4, "one scale group per pass over the weight ring");
     u4_t wslot[DW][NBW];
     uint32_t eslot[DW][NBW];
     u4_t xslot[DX][XP];
@@ -110,8 +118,16 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__re
             const bool ok = segok && tok[s];
             w[s] = __builtin_bit_cast(u4_t,
                                       __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? wrow[s] + 64u * c : kOob, 0, 0));
-            e[s] = __builtin_amdgcn_raw_buffer_load_b8(re, ok ? erow[s] + 4u * c : kOob, 0, 0);
+            if constexpr (!SV) e[s] = __builtin_amdgcn_raw_buffer_load_b8(re, ok ? erow[s] + 4u * c : kOob, 0, 0);
         }
+    };
+    // scales of chunks 4G .. 4G+3 (rows past N and groups past the row end
+    // read zeros or the next row's bytes; neither is ever multiplied)
+    auto load_sv = [&](u4_t (&v)[NBW], int G) {
+#pragma unroll
+        for (int s = 0; s < NBW; ++s)
+            v[s] = __builtin_bit_cast(
+                u4_t, __builtin_amdgcn_raw_buffer_load_b128(re, tok[s] ? erow0[s] + 16u * (uint32_t)G : kOob, 0, 0));
     };
     auto load_x = [&](u4_t (&xv)[XP], int c) {
 #pragma unroll
@@ -169,10 +185,12 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__re
     // buffer c & 1 while it is multiplied, and chunks c+1 .. c+DX wait in the
     // register slots xslot[(c+1) % DX] ...
     // Prologue: chunk 0's activations to LDS, chunks 1..DX in registers,
-    // weights of chunks 0..DW-1 in flight.
+    // weights of chunks 0..DW-1 (and their scale group) in flight.
+    u4_t svc[SV ? NBW : 1], svn[SV ? NBW : 1];
     load_x(xslot[0], 0);
 #pragma unroll
     for (int d = 0; d < DW; ++d) load_w(wslot[d], eslot[d], d);
+    if constexpr (SV) load_sv(svn, 0);
     publish(xslot[0], 0);
 #pragma unroll
     for (int d = 1; d <= DX; ++d) load_x(xslot[d % DX], d);
@@ -189,11 +207,22 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__re
 #pragma unroll
         for (int d = 0; d < DW; ++d) {
             const int c = c0 + d;
+            if constexpr (SV) {
+                if (d == 0) {
+#pragma unroll
+                    for (int s = 0; s < NBW; ++s) svc[s] = svn[s];
+                }
+#pragma unroll
+                for (int s = 0; s < NBW; ++s) eslot[d][s] = (svc[s][d] >> (8 * g)) & 0xFFu;
+            }
             if (c < nchunk) multiply(wslot[d], eslot[d], c);
             u4_t(&nx)[XP] = xslot[(d + 1) % DX];
             publish(nx, c + 1);
             load_x(nx, c + 1 + DX);
             load_w(wslot[d], eslot[d], c + DW);
+            if constexpr (SV) {
+                if (d == 0) load_sv(svn, c / 4 + 1);
+            }
             __syncthreads();
         }
     }
@@ -213,14 +242,14 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__re
     }
 }
 
-// Prefetch depths in chunks, measured on MI355X: weights (from HBM) six
-// chunks ahead up to 64 rows (bound by HBM) and four above; activations
-// (mostly L2 hits) two ahead.  Each iteration issues its activation loads
+// Prefetch depths in chunks, measured on MI355X: weights (from HBM) four
+// chunks ahead (six measured the same up to 64 rows, eight slower);
+// activations (mostly L2 hits) two ahead.  Each iteration issues its activation loads
 // before its weight loads: a wave's loads complete in issue order, so the
 // wait for an activation chunk only covers older weight loads.  Above 64
 // rows M is split into blocks of MT_L = 4 m-tiles.
 #ifndef QMV_MFMA_DW_S
-#define QMV_MFMA_DW_S 6
+#define QMV_MFMA_DW_S 4
 #endif
 #ifndef QMV_MFMA_DW_L
 #define QMV_MFMA_DW_L 4
@@ -234,9 +263,15 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mxfp4_mfma(const uint8_t *__re
 
 template <int MT, int NBW, int DW>
 static hipError_t mfma_launch(const MatvecArgs &a, int NT, int ranges, int mblocks, hipStream_t st) {
-    hipLaunchKernelGGL((k_mxfp4_mfma<MT, NBW, DW, QMV_MFMA_DX>), dim3(ranges, mblocks), dim3(kMfmaThreads), 0, st,
-                       reinterpret_cast<const uint8_t *>(a.wq), reinterpret_cast<const uint8_t *>(a.sc), a.x,
-                       a.y, a.y_dtype, a.M, a.N, a.K, NT, ranges);
+    const dim3 grid(ranges, mblocks);
+    const auto *wq = reinterpret_cast<const uint8_t *>(a.wq);
+    const auto *sc = reinterpret_cast<const uint8_t *>(a.sc);
+    if (a.K % 128 == 0)
+        hipLaunchKernelGGL((k_mxfp4_mfma<MT, NBW, DW, QMV_MFMA_DX, true>), grid, dim3(kMfmaThreads), 0, st, wq, sc,
+                           a.x, a.y, a.y_dtype, a.M, a.N, a.K, NT, ranges);
+    else
+        hipLaunchKernelGGL((k_mxfp4_mfma<MT, NBW, DW, QMV_MFMA_DX, false>), grid, dim3(kMfmaThreads), 0, st, wq,
+                           sc, a.x, a.y, a.y_dtype, a.M, a.N, a.K, NT, ranges);
     return hipGetLastError();
 }
 
