@@ -80,6 +80,10 @@ def test_workload5_mfma_sampled_rows(M):
     (255, 64, 8192),
     (256, 2049, 512),
     (32, 40000, 256),    # more tiles than 256 workgroups x 8: extra workgroups
+    # K a multiple of 128: one 16-byte scale load per tile covers four chunks
+    (32, 17, 128),       # the last row's scale group runs past the end of the scales
+    (40, 33, 384),       # 33 x 12 scale bytes: the last group straddles the end
+    (64, 1, 1152),       # a single weight row
 ])
 def test_mfma_shapes(M, N, K):
     d = synth.mxfp4_inputs(M, N, K, salt=M + N + K)
