@@ -35,6 +35,7 @@ Only the CPU-baseline legs use the oracle.
 import argparse
 import ctypes
 import hashlib
+import importlib.util
 import json
 import os
 import statistics
@@ -95,14 +96,26 @@ def strip_comments(src):
     return " ".join("".join(out).split())
 
 
+def build_flags():
+    """The product library's compile flags (the build script's FLAGS), without
+    include paths, which differ between checkouts."""
+    spec = importlib.util.spec_from_file_location("_qmv_build", os.path.join(ROOT, "skinny_gemm_qmv_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return [f for f in mod.FLAGS if not f.startswith("-I")]
+
+
 def source_digest():
-    """Digest of the product library's HIP sources, comments left out, to tell
+    """Digest of what the product library is built from -- its HIP sources and
+    public header with comments left out, and its compile flags -- to tell
     whether stored counter readings still describe the kernels being timed."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "skinny_gemm_qmv_amd", "csrc")
-    for name in DIGEST_FILES:
-        with open(os.path.join(csrc, name), encoding="utf-8") as f:
-            h.update(name.encode() + strip_comments(f.read()).encode())
+    paths = [os.path.join(csrc, name) for name in DIGEST_FILES] + [os.path.join(ROOT, "include", "qmv.h")]
+    for path in paths:
+        with open(path, encoding="utf-8") as f:
+            h.update(os.path.basename(path).encode() + strip_comments(f.read()).encode())
+    h.update(" ".join(build_flags()).encode())
     return h.hexdigest()[:16]
 
 

@@ -46,6 +46,26 @@ def test_digest_ignores_comments_but_not_code():
     assert bench.strip_comments(src) != bench.strip_comments(src.replace("x // y", "x // z"))  # in a string
 
 
+def test_digest_covers_the_header_and_the_compile_flags(monkeypatch):
+    flags = bench.build_flags()
+    assert "-ffp-contract=off" in flags and "--offload-arch=gfx950" in flags
+    assert not any(f.startswith("-I") for f in flags)   # paths differ between checkouts
+    base = bench.source_digest()
+    monkeypatch.setattr(bench, "build_flags", lambda: flags + ["-ffast-math"])
+    assert bench.source_digest() != base
+    monkeypatch.setattr(bench, "build_flags", lambda: flags)
+    real_open = open
+
+    def header_changed(path, *a, **k):
+        if str(path).endswith(os.path.join("include", "qmv.h")):
+            import io
+            with real_open(path, *a, **k) as f:
+                return io.StringIO(f.read() + "\nint qmv_extra_declaration;\n")
+        return real_open(path, *a, **k)
+    monkeypatch.setattr("builtins.open", header_changed)
+    assert bench.source_digest() != base
+
+
 def test_stored_traffic_follows_the_digest(tmp_path, monkeypatch):
     rec = {"source_digest": "0123456789abcdef", "hbm_bytes_per_launch": 12345}
     (tmp_path / "t.json").write_text(json.dumps(rec))
